@@ -1,0 +1,206 @@
+/*
+ * pa.h -- paged attention on AMD Instinct MI355X (gfx950): the C ABI of libpa.so.
+ *
+ * The operations follow the pages that describe PagedAttention:
+ *  - "Inside vLLM v0.7: How PagedAttention & Chunked Prefill Scaled 10x Token Serving"
+ *    (bicarait.com), "Architectural Blueprint 2" (fixed-size blocks of 16 or 32 tokens,
+ *    a block table from logical block index to physical frame, frames shared by
+ *    pointer) and "Architectural Blueprint 3" (512-token prefill chunks run in the same
+ *    iteration as decodes).
+ *  - "Inside vLLM Architecture" (codebumble.net), "Architectural Anatomy" (the kernel
+ *    gathers non-contiguous K/V while computing QK^T), "The Block Table Mapping
+ *    Subsystem" (a position splits into logical block = pos / block_size and offset =
+ *    pos % block_size), "CUDA Shared Memory Optimization" (coalesced per-block fetches,
+ *    partial softmax results merged by a final normalised reduction), and its FAQ
+ *    (PagedAttention is exact attention; only addressing changes).
+ *  - "High-Throughput LLM Serving with vLLM & PagedAttention" (infoisland), section 2
+ *    (branches share prompt blocks; copy-on-write when they diverge) and section 4
+ *    (an fp8 KV cache).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every data pointer is a device pointer (memory of the current HIP device)
+ *   except in the pa_validate_* functions, which read host memory only.  The caller
+ *   owns all memory.  The library allocates nothing and keeps no state besides the
+ *   thread-local error message.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
+ *   call enqueues its kernels on that stream and returns without synchronising.
+ * Errors.  Each call returns PA_OK or a negative status; pa_last_error() then holds a
+ *   message.  Scalar arguments (sizes, dtypes, null pointers, workspace size) are always
+ *   checked before anything is launched.  The contents of index arrays (block tables,
+ *   context lengths, slots, copy pairs) live on the device and are NOT read by the
+ *   entry points; check them with the pa_validate_* functions on a host copy.  The
+ *   kernels never access memory outside the buffers the arguments describe, even for
+ *   invalid indices: a frame id outside [0, NB) is skipped, a context length is clamped
+ *   to [0, min(max_context_len, max_blocks_per_seq * block_size)], a slot outside
+ *   [0, NB * block_size) is skipped.  Results for such inputs are unspecified.
+ * Shapes.  Hq query heads share Hkv KV heads in groups of G = Hq / Hkv: query head h
+ *   reads KV head h / G.  Supported: D (head_dim) in {64, 128}, block_size in {16, 32},
+ *   G in {1, 2, 4, 8, 16}, and (q, kv, out) dtypes (f32, f32, f32), (bf16, bf16, bf16),
+ *   (bf16, fp8, bf16).  Accumulation is fp32; outputs are rounded to nearest even.
+ *
+ * KV cache layout
+ * ---------------
+ * k_cache and v_cache each hold NB frames; frame f holds Hkv tiles, the tile of KV head
+ * g starting at element (f * Hkv + g) * block_size * D.  A tile holds the block_size
+ * tokens of the frame for one head; token slot o (0 <= o < block_size) of frame f is
+ * slot number f * block_size + o.  Inside a tile, with b = bytes per element, the
+ * value of slot o and head-dim index d sits at byte
+ *   K:  h = o / 16, kl = o % 16, j = d / (D/4), t = d % (D/4)
+ *       byte = 1024 * (h * (D*b/64) + (t*b) / 16) + 16 * (16*j + kl) + (t*b) % 16
+ *   V:  h = o / 16, j = (o % 16) / 4, i = o % 4, c = d / 16, dl = d % 16,
+ *       u = h * (D/16) + c, Q = 4 / b
+ *       byte = 1024 * (u / Q) + 16 * (16*j + dl) + (4 * (u % Q) + i) * b
+ * i.e. a tile is a sequence of 1 KiB pieces, each 64 lanes x 16 bytes, and each lane's
+ * 16 bytes are exactly what one lane of a 64-wide wavefront feeds a matrix-core
+ * instruction: every gather of a tile is a run of fully contiguous 1 KiB loads.
+ * fp8 values are OCP e4m3fn codes; a stored code c means value(c) * scale with the
+ * per-tensor k_scale (v_scale) of the cache.  Write the caches only through
+ * pa_reshape_and_cache (and copy frames with pa_copy_blocks).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8_E4M3 = 2 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,  /* null pointer, bad size, or an index array that fails validation */
+  PA_ERANGE = -2,  /* a value outside its allowed range (validators) */
+  PA_ENOTSUP = -3, /* a shape or dtype combination this build does not implement */
+  PA_EHIP = -4,    /* a HIP runtime call or kernel launch failed */
+  PA_ENOSPC = -5   /* the workspace is smaller than the *_workspace_bytes result */
+};
+
+/* Message describing the last failure on the calling thread ("" after success). */
+const char* pa_last_error(void);
+
+/* Library version and the GPU architecture its kernels are built for. */
+const char* pa_build_info(void);
+
+/*
+ * pa_reshape_and_cache -- store this step's new K and V rows in their cache slots.
+ * Defined by the block-table mapping (codebumble.net, "The Block Table Mapping
+ * Subsystem"): token i goes to frame slot_mapping[i] / block_size at offset
+ * slot_mapping[i] % block_size, for every KV head.
+ *   k, v          [T, Hkv, D] rows in src_dtype (f32 or bf16), contiguous.
+ *   k_cache, v_cache  caches in kv_dtype, layout above, written in place.
+ *   slot_mapping  int64 [T]; a negative slot skips the token (padding).  Two tokens must
+ *                 not name the same slot in one call (the later write is unspecified).
+ *   kv_dtype      f32 from f32 and bf16 from bf16 store the bits unchanged; fp8 from
+ *                 bf16 stores e4m3fn(RNE, saturating to +-448)(fp32(x) / scale), with
+ *                 scale = k_scale for K and v_scale for V (NaN stays NaN).
+ */
+int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t T, int64_t NB, int Hkv, int D,
+                         int block_size, pa_dtype src_dtype, pa_dtype kv_dtype, float k_scale,
+                         float v_scale, void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write support (infoisland, section 2): for every pair
+ * (src, dst) of `pairs` (int64 [N][2]) frame dst of both caches becomes a bit copy of
+ * frame src (all Hkv tiles).  Destinations must be distinct and none may be a source;
+ * the copies then do not depend on their order.  A pair with an index outside [0, NB)
+ * is skipped.
+ */
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int64_t N, int64_t NB,
+                   int Hkv, int D, int block_size, pa_dtype kv_dtype, void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for this batch shape (0 is a valid answer:
+ * then workspace may be NULL).  max_context_len bounds every context_lens entry.
+ */
+size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype kv_dtype,
+                                 int max_context_len);
+
+/*
+ * pa_decode -- one decode step of paged attention (codebumble.net, "Architectural
+ * Anatomy" and FAQ; bicarait.com, "Architectural Blueprint 2"):
+ *   out[b, h, :] = sum_t softmax_t(scale * q[b, h, :] . K_b[t, h/G, :]) V_b[t, h/G, :]
+ * over t < context_lens[b], where K_b[t] and V_b[t] are read from frame
+ * block_tables[b, t / block_size], slot t % block_size, dequantised for fp8.
+ *   out, q        [B, Hq, D] in q_dtype (out has the q dtype), contiguous.
+ *   block_tables  int32 [B, max_blocks_per_seq]; entries past ceil(L/block_size) unused.
+ *   context_lens  int32 [B], each in [1, max_context_len]; the count includes the token
+ *                 written this step (write it with pa_reshape_and_cache first, on the
+ *                 same stream).
+ *   max_context_len  host-side bound on the lengths; sizes the launch grid.
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, used
+ *                 for the partial results of long contexts (split across the context and
+ *                 merged by a second reduce kernel).  Not read before it is written.
+ * Long contexts are split into partitions processed in parallel; the merge is exact up
+ * to fp32 rounding.  Concurrent calls must not share a workspace.
+ */
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+              pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+              int max_context_len, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace pa_prefill_chunk needs for these bounds (0 is a valid answer:
+ * then workspace may be NULL).  The arguments are the ones pa_prefill_chunk receives. */
+size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
+                                        int max_context_len, int Hq, int Hkv, int D,
+                                        int block_size, pa_dtype kv_dtype);
+
+/*
+ * pa_prefill_chunk -- causal attention of prefill chunks over their paged context
+ * (bicarait.com, "Architectural Blueprint 3"; infoisland, section 5).  Chunk c owns the
+ * query rows r in [query_start_loc[c], query_start_loc[c+1]) (C_c rows); its sequence has
+ * L_c = context_lens[c] tokens including the chunk, so row i of the chunk sits at
+ * position L_c - C_c + i and attends keys 0 .. L_c - C_c + i (inclusive) through
+ * block_tables[c]:
+ *   out[r, h, :] = sum_{t <= pos} softmax_t(scale * q[r, h, :] . K[t, h/G, :]) V[t, h/G, :].
+ *   out, q           [total_q, Hq, D] in q_dtype, contiguous; total_q = query_start_loc[num_chunks].
+ *   query_start_loc  int32 [num_chunks + 1], non-decreasing, starting at 0.
+ *   context_lens     int32 [num_chunks], C_c <= L_c <= max_context_len.
+ *   max_chunk_len    host-side bound on C_c; sizes the grid together with max_context_len.
+ *   workspace        at least pa_prefill_chunk_workspace_bytes(...) bytes.
+ * The chunk's own K/V must already be in the cache (pa_reshape_and_cache on the same
+ * stream).
+ */
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* query_start_loc, const int32_t* context_lens, int num_chunks,
+                     int64_t total_q, int max_chunk_len, int max_context_len, int Hq, int Hkv,
+                     int D, int block_size, int64_t NB, float scale, pa_dtype q_dtype,
+                     pa_dtype kv_dtype, float k_scale, float v_scale, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * Host-side validators (no GPU needed).  Each returns PA_OK or PA_EINVAL/PA_ERANGE with
+ * pa_last_error() naming the first offending entry.
+ *  pa_validate_decode_indices: 1 <= context_lens[b] <= min(max_context_len,
+ *    max_blocks_per_seq * block_size) and 0 <= block_tables[b, i] < NB for every
+ *    i < ceil(context_lens[b] / block_size).
+ *  pa_validate_slots: every slot is negative (skip) or in [0, NB * block_size), and no
+ *    non-negative slot repeats.
+ *  pa_validate_copy_pairs: every index in [0, NB), destinations distinct, no destination
+ *    is also a source.
+ *  pa_validate_chunk_indices: query_start_loc starts at 0 and does not decrease, every
+ *    chunk length is at most max_chunk_len and at most its context length, context
+ *    lengths are in [1, max_context_len], and the table entries the context covers are
+ *    in [0, NB).
+ */
+int pa_validate_decode_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int B, int block_size, int64_t NB,
+                               int max_context_len);
+int pa_validate_slots(const int64_t* slot_mapping, int64_t T, int64_t NB, int block_size);
+int pa_validate_copy_pairs(const int64_t* pairs, int64_t N, int64_t NB);
+int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int num_chunks, int block_size, int64_t NB, int max_chunk_len,
+                              int max_context_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

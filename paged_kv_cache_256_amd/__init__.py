@@ -1,0 +1,31 @@
+"""MI355X-native paged attention: hand-written gfx950 HIP kernels behind a C ABI (libpa.so).
+
+The Python layer only marshals torch tensors (device memory, streams) into the C entry points
+declared in include/pa.h:
+
+    reshape_and_cache  write this step's K/V rows into their cache slots
+    copy_blocks        duplicate frames for copy-on-write
+    decode             paged GQA decode attention (split over the context + reduce)
+    prefill_chunk      causal attention of prefill chunks over their paged context
+"""
+
+from ._binding import (  # noqa: F401
+    EXPORTED,
+    LIB_PATH,
+    PAError,
+    build_info,
+    copy_blocks,
+    decode,
+    decode_workspace_bytes,
+    last_error,
+    lib,
+    new_kv_cache,
+    prefill_chunk,
+    prefill_chunk_workspace_bytes,
+    q_dtype_for,
+    reshape_and_cache,
+    validate_chunk_indices,
+    validate_copy_pairs,
+    validate_decode_indices,
+    validate_slots,
+)

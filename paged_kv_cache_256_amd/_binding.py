@@ -1,0 +1,250 @@
+"""ctypes binding of libpa.so: argument marshalling only.
+
+Every computation runs in the library's HIP kernels.  Tensors are torch tensors on the
+current GPU (torch supplies device memory and streams); the binding checks device,
+dtype, shape and contiguity, passes raw pointers and the current stream, and raises
+PAError for a nonzero status.  If libpa.so has not been built the import of this module
+fails: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loaded first: libpa.so then binds to the HIP runtime torch already loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+DTYPE_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+STATUS = {0: "PA_OK", -1: "PA_EINVAL", -2: "PA_ERANGE", -3: "PA_ENOTSUP", -4: "PA_EHIP",
+          -5: "PA_ENOSPC"}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_256_amd.build`"
+                      " (there is no fallback implementation)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+_SIGS = {
+    "pa_last_error": ([], ctypes.c_char_p),
+    "pa_build_info": ([], ctypes.c_char_p),
+    "pa_reshape_and_cache": ([_P, _P, _P, _P, _P, _I64, _I64, _I, _I, _I, _I, _I, _F, _F, _P], _I),
+    "pa_copy_blocks": ([_P, _P, _P, _I64, _I64, _I, _I, _I, _I, _P], _I),
+    "pa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "pa_decode": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F, _F, _I,
+                   _P, _SZ, _P], _I),
+    "pa_prefill_chunk_workspace_bytes": ([_I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "pa_prefill_chunk": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I64,
+                          _F, _I, _I, _F, _F, _P, _SZ, _P], _I),
+    "pa_validate_decode_indices": ([_P, _I, _P, _I, _I, _I64, _I], _I),
+    "pa_validate_slots": ([_P, _I64, _I64, _I], _I),
+    "pa_validate_copy_pairs": ([_P, _I64, _I64], _I),
+    "pa_validate_chunk_indices": ([_P, _I, _P, _P, _I, _I, _I64, _I, _I], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.argtypes = _args
+    _fn.restype = _res
+
+EXPORTED = tuple(_SIGS)
+
+
+def lib():
+    return _lib
+
+
+def last_error() -> str:
+    return _lib.pa_last_error().decode()
+
+
+def build_info() -> str:
+    return _lib.pa_build_info().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise PAError(status, last_error())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _cache_geometry(k_cache, v_cache, block_size, kv_dtype):
+    if k_cache.shape != v_cache.shape or k_cache.dim() != 3:
+        raise ValueError("k_cache and v_cache must both be [NB, Hkv, block_size*D]")
+    NB, Hkv, tile = k_cache.shape
+    if tile % block_size:
+        raise ValueError("cache tile size is not a multiple of block_size")
+    return NB, Hkv, tile // block_size
+
+
+def new_kv_cache(NB: int, Hkv: int, block_size: int, D: int, kv_dtype: str, device="cuda"):
+    """Empty K and V caches [NB, Hkv, block_size*D] (layout defined in include/pa.h)."""
+    shape = (NB, Hkv, block_size * D)
+    return (torch.empty(shape, dtype=TORCH_DTYPE[kv_dtype], device=device),
+            torch.empty(shape, dtype=TORCH_DTYPE[kv_dtype], device=device))
+
+
+def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, block_size: int, kv_dtype: str,
+                      k_scale: float = 1.0, v_scale: float = 1.0):
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    src = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k.dtype)
+    if src is None or v.dtype != k.dtype:
+        raise TypeError("k and v must both be float32 or bfloat16")
+    T = k.shape[0]
+    if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D):
+        raise ValueError(f"k, v must be [T, {Hkv}, {D}]")
+    args = (_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, Hkv, D, block_size,
+            DTYPE_CODE[src], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), _stream(k))
+    _check(_lib.pa_reshape_and_cache(*args))
+
+
+def copy_blocks(k_cache, v_cache, pairs, *, block_size: int, kv_dtype: str):
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    if pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be [N, 2]")
+    _check(_lib.pa_copy_blocks(_dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+                               _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+                               _dev(pairs, "pairs", torch.int64), pairs.shape[0], NB, Hkv, D,
+                               block_size, DTYPE_CODE[kv_dtype], _stream(k_cache)))
+
+
+def decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len) -> int:
+    return int(_lib.pa_decode_workspace_bytes(B, Hq, D, block_size, DTYPE_CODE[kv_dtype],
+                                              max_context_len))
+
+
+def q_dtype_for(kv_dtype: str) -> str:
+    return "f32" if kv_dtype == "f32" else "bf16"
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, scale: float,
+           kv_dtype: str, max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
+           out=None, workspace=None):
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    qd = q_dtype_for(kv_dtype)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    if out is None:
+        out = torch.empty_like(q)
+    need = decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if os.environ.get("PA_VALIDATE") == "1":
+        validate_decode_indices(block_tables.cpu().numpy(), context_lens.cpu().numpy(),
+                                block_size, NB, max_context_len)
+    _check(_lib.pa_decode(_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+                          _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+                          _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+                          _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+                          _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D,
+                          block_size, NB, float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype],
+                          float(k_scale), float(v_scale), int(max_context_len), ws, wsb,
+                          _stream(q)))
+    return out
+
+
+def prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,
+                                  D, block_size, kv_dtype) -> int:
+    return int(_lib.pa_prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len,
+                                                     max_context_len, Hq, Hkv, D, block_size,
+                                                     DTYPE_CODE[kv_dtype]))
+
+
+def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, *,
+                  block_size: int, scale: float, kv_dtype: str, max_chunk_len: int,
+                  max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, out=None,
+                  workspace=None):
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    qd = q_dtype_for(kv_dtype)
+    total_q, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    num_chunks = context_lens.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    need = prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq,
+                                         Hkv, D, block_size, kv_dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if os.environ.get("PA_VALIDATE") == "1":
+        validate_chunk_indices(block_tables.cpu().numpy(), query_start_loc.cpu().numpy(),
+                               context_lens.cpu().numpy(), block_size, NB, max_chunk_len,
+                               max_context_len)
+    _check(_lib.pa_prefill_chunk(
+        _dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+        _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]), _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(context_lens, "context_lens", torch.int32, 1), num_chunks, total_q, int(max_chunk_len),
+        int(max_context_len), Hq, Hkv, D, block_size, NB, float(scale), DTYPE_CODE[qd],
+        DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), ws, wsb, _stream(q)))
+    return out
+
+
+# ----------------------------------------------------------------------------- host validators
+
+
+def _host(a, dtype):
+    a = np.ascontiguousarray(np.asarray(a, dtype=dtype))
+    return a, ctypes.c_void_p(a.ctypes.data)
+
+
+def validate_decode_indices(block_tables, context_lens, block_size, NB, max_context_len):
+    bt, pbt = _host(block_tables, np.int32)
+    cl, pcl = _host(context_lens, np.int32)
+    _check(_lib.pa_validate_decode_indices(pbt, bt.shape[1], pcl, cl.shape[0], block_size, NB,
+                                           int(max_context_len)))
+
+
+def validate_slots(slot_mapping, NB, block_size):
+    s, ps = _host(slot_mapping, np.int64)
+    _check(_lib.pa_validate_slots(ps, s.shape[0], NB, block_size))
+
+
+def validate_copy_pairs(pairs, NB):
+    p, pp = _host(np.asarray(pairs).reshape(-1, 2), np.int64)
+    _check(_lib.pa_validate_copy_pairs(pp, p.shape[0], NB))
+
+
+def validate_chunk_indices(block_tables, query_start_loc, context_lens, block_size, NB,
+                           max_chunk_len, max_context_len):
+    bt, pbt = _host(block_tables, np.int32)
+    qs, pqs = _host(query_start_loc, np.int32)
+    cl, pcl = _host(context_lens, np.int32)
+    _check(_lib.pa_validate_chunk_indices(pbt, bt.shape[1], pqs, pcl, cl.shape[0], block_size, NB,
+                                          int(max_chunk_len), int(max_context_len)))

@@ -1,0 +1,274 @@
+// pa_api.cpp -- the C ABI of libpa.so: argument checks, dispatch to the launchers, host-side
+// validators and the thread-local error message.  No exception crosses the ABI.
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/pa.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+int ok() {
+  g_error.clear();
+  return PA_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool valid_dtype(int d) { return d == PA_F32 || d == PA_BF16 || d == PA_FP8_E4M3; }
+int elem_bytes(int d) { return d == PA_F32 ? 4 : (d == PA_BF16 ? 2 : 1); }
+
+// Shapes the kernels are built for.
+int check_shape(int D, int bs, int kv_dtype) {
+  if (D != 64 && D != 128) return fail(PA_ENOTSUP, "head_dim %d not supported (64 or 128)", D);
+  if (bs != 16 && bs != 32) return fail(PA_ENOTSUP, "block_size %d not supported (16 or 32)", bs);
+  if (!valid_dtype(kv_dtype)) return fail(PA_EINVAL, "unknown kv dtype %d", kv_dtype);
+  if (kv_dtype == PA_F32 && D == 128 && bs == 32)
+    return fail(PA_ENOTSUP, "f32 cache with head_dim 128 and block_size 32 not supported");
+  return PA_OK;
+}
+
+int check_heads(int Hq, int Hkv) {
+  if (Hq < 1 || Hkv < 1) return fail(PA_EINVAL, "head counts must be positive (Hq %d, Hkv %d)", Hq, Hkv);
+  if (Hq % Hkv) return fail(PA_EINVAL, "Hq %d is not a multiple of Hkv %d", Hq, Hkv);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(PA_ENOTSUP, "query heads per kv head %d not supported (1, 2, 4, 8, 16)", G);
+  if (Hkv > 65535) return fail(PA_ENOTSUP, "Hkv %d too large", Hkv);
+  return PA_OK;
+}
+
+int check_attn_dtypes(int q_dtype, int kv_dtype) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype))
+    return fail(PA_EINVAL, "unknown dtype (q %d, kv %d)", q_dtype, kv_dtype);
+  const bool okc = (q_dtype == PA_F32 && kv_dtype == PA_F32) ||
+                   (q_dtype == PA_BF16 && kv_dtype == PA_BF16) ||
+                   (q_dtype == PA_BF16 && kv_dtype == PA_FP8_E4M3);
+  if (!okc) return fail(PA_ENOTSUP, "dtype combination q %d / kv %d not supported", q_dtype, kv_dtype);
+  return PA_OK;
+}
+
+int check_scales(int kv_dtype, float k_scale, float v_scale) {
+  if (kv_dtype != PA_FP8_E4M3) return PA_OK;
+  if (!(std::isfinite(k_scale) && k_scale > 0.f && std::isfinite(v_scale) && v_scale > 0.f))
+    return fail(PA_EINVAL, "fp8 scales must be finite and positive (k %g, v %g)", k_scale, v_scale);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_last_error(void) { return g_error.c_str(); }
+
+const char* pa_build_info(void) { return "libpa 0.1 (paged attention), kernels for gfx950"; }
+
+int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int64_t T, int64_t NB, int Hkv, int D,
+                         int block_size, pa_dtype src_dtype, pa_dtype kv_dtype, float k_scale,
+                         float v_scale, void* stream) {
+  if (T < 0 || NB < 1 || Hkv < 1) return fail(PA_EINVAL, "bad sizes (T %lld, NB %lld, Hkv %d)", (long long)T, (long long)NB, Hkv);
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (!valid_dtype(src_dtype) || src_dtype == PA_FP8_E4M3)
+    return fail(PA_EINVAL, "source dtype %d must be f32 or bf16", (int)src_dtype);
+  const bool okc = (kv_dtype == src_dtype) || kv_dtype == PA_FP8_E4M3;
+  if (!okc) return fail(PA_ENOTSUP, "storing dtype %d rows in a dtype %d cache not supported", (int)src_dtype, (int)kv_dtype);
+  if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
+  if (T > 0x7fffffff) return fail(PA_ENOTSUP, "T %lld too large for one call", (long long)T);
+  if (T == 0) return ok();
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_EINVAL, "null pointer argument");
+  return hip_status(pa::launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, T, NB, Hkv, D,
+                                                 block_size, src_dtype, kv_dtype, k_scale, v_scale,
+                                                 (hipStream_t)stream),
+                    "reshape_and_cache launch");
+}
+
+int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int64_t N, int64_t NB,
+                   int Hkv, int D, int block_size, pa_dtype kv_dtype, void* stream) {
+  if (N < 0 || NB < 1 || Hkv < 1) return fail(PA_EINVAL, "bad sizes (N %lld, NB %lld, Hkv %d)", (long long)N, (long long)NB, Hkv);
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (N > 0x7fffffff) return fail(PA_ENOTSUP, "N %lld too large for one call", (long long)N);
+  if (N == 0) return ok();
+  if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "null pointer argument");
+  const int64_t frame_bytes = (int64_t)Hkv * block_size * D * elem_bytes(kv_dtype);
+  return hip_status(pa::launch_copy_blocks(k_cache, v_cache, pairs, N, NB, frame_bytes, (hipStream_t)stream),
+                    "copy_blocks launch");
+}
+
+size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype kv_dtype,
+                                 int max_context_len) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_context_len <= 0) return 0;
+  return pa::decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len);
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+              pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+              int max_context_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || NB < 1 || max_blocks_per_seq < 1)
+    return fail(PA_EINVAL, "bad sizes (B %d, NB %lld, max_blocks_per_seq %d)", B, (long long)NB, max_blocks_per_seq);
+  if (B > 65535) return fail(PA_ENOTSUP, "batch %d too large for one call (max 65535)", B);
+  if (int r = check_heads(Hq, Hkv)) return r;
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (int r = check_attn_dtypes(q_dtype, kv_dtype)) return r;
+  if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (B == 0) return ok();
+  if (max_context_len < 1) return fail(PA_EINVAL, "max_context_len %d must be positive", max_context_len);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_EINVAL, "null pointer argument");
+  const size_t need = pa::decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  pa::DecodeParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     B, Hq, Hkv, D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
+                     max_context_len, need > 0 ? workspace : nullptr};
+  return hip_status(pa::launch_decode(p, (hipStream_t)stream), "decode launch");
+}
+
+size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
+                                        int max_context_len, int Hq, int Hkv, int D,
+                                        int block_size, pa_dtype kv_dtype) {
+  (void)block_size;
+  if (num_chunks <= 0 || total_q <= 0 || max_chunk_len <= 0 || max_context_len <= 0 || Hq <= 0 ||
+      Hkv <= 0 || D <= 0 || Hq % Hkv)
+    return 0;
+  return pa::prefill_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D, (int)kv_dtype);
+}
+
+int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* query_start_loc, const int32_t* context_lens, int num_chunks,
+                     int64_t total_q, int max_chunk_len, int max_context_len, int Hq, int Hkv,
+                     int D, int block_size, int64_t NB, float scale, pa_dtype q_dtype,
+                     pa_dtype kv_dtype, float k_scale, float v_scale, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (num_chunks < 0 || total_q < 0 || NB < 1 || max_blocks_per_seq < 1)
+    return fail(PA_EINVAL, "bad sizes (num_chunks %d, total_q %lld, NB %lld)", num_chunks, (long long)total_q, (long long)NB);
+  if (int r = check_heads(Hq, Hkv)) return r;
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (int r = check_attn_dtypes(q_dtype, kv_dtype)) return r;
+  if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (num_chunks == 0 || total_q == 0) return ok();
+  if (max_chunk_len < 1 || max_context_len < max_chunk_len)
+    return fail(PA_EINVAL, "need 1 <= max_chunk_len (%d) <= max_context_len (%d)", max_chunk_len, max_context_len);
+  if (total_q > 0x7fffffff) return fail(PA_ENOTSUP, "total_q %lld too large", (long long)total_q);
+  if ((long long)num_chunks * Hkv > 65535) return fail(PA_ENOTSUP, "num_chunks * Hkv too large (max 65535)");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+    return fail(PA_EINVAL, "null pointer argument");
+  const size_t need = pa::prefill_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D, (int)kv_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  pa::PrefillParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, query_start_loc,
+                      context_lens, num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,
+                      D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
+                      need > 0 ? workspace : nullptr};
+  return hip_status(pa::launch_prefill(p, (hipStream_t)stream), "prefill_chunk launch");
+}
+
+// ----------------------------------------------------------------------------- validators
+
+int pa_validate_decode_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                               const int32_t* context_lens, int B, int block_size, int64_t NB,
+                               int max_context_len) {
+  if (B < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1) return fail(PA_EINVAL, "bad sizes");
+  if (B > 0 && (!block_tables || !context_lens)) return fail(PA_EINVAL, "null pointer argument");
+  const long long cap = std::min<long long>(max_context_len, (long long)max_blocks_per_seq * block_size);
+  for (int b = 0; b < B; ++b) {
+    const int L = context_lens[b];
+    if (L < 1 || L > cap)
+      return fail(PA_ERANGE, "context_lens[%d] = %d outside [1, %lld]", b, L, cap);
+    const int nblk = (L + block_size - 1) / block_size;
+    for (int i = 0; i < nblk; ++i) {
+      const int32_t f = block_tables[(size_t)b * max_blocks_per_seq + i];
+      if (f < 0 || f >= NB)
+        return fail(PA_ERANGE, "block_tables[%d][%d] = %d outside [0, %lld)", b, i, f, (long long)NB);
+    }
+  }
+  return ok();
+}
+
+int pa_validate_slots(const int64_t* slot_mapping, int64_t T, int64_t NB, int block_size) {
+  if (T < 0 || NB < 1 || block_size < 1) return fail(PA_EINVAL, "bad sizes");
+  if (T > 0 && !slot_mapping) return fail(PA_EINVAL, "null pointer argument");
+  const int64_t nslots = NB * block_size;
+  std::unordered_set<int64_t> seen;
+  seen.reserve((size_t)T);
+  for (int64_t i = 0; i < T; ++i) {
+    const int64_t s = slot_mapping[i];
+    if (s < 0) continue;
+    if (s >= nslots)
+      return fail(PA_ERANGE, "slot_mapping[%lld] = %lld outside [0, %lld)", (long long)i, (long long)s, (long long)nslots);
+    if (!seen.insert(s).second)
+      return fail(PA_EINVAL, "slot %lld written twice (slot_mapping[%lld])", (long long)s, (long long)i);
+  }
+  return ok();
+}
+
+int pa_validate_copy_pairs(const int64_t* pairs, int64_t N, int64_t NB) {
+  if (N < 0 || NB < 1) return fail(PA_EINVAL, "bad sizes");
+  if (N > 0 && !pairs) return fail(PA_EINVAL, "null pointer argument");
+  std::unordered_set<int64_t> src, dst;
+  for (int64_t i = 0; i < N; ++i) {
+    const int64_t s = pairs[2 * i], d = pairs[2 * i + 1];
+    if (s < 0 || s >= NB || d < 0 || d >= NB)
+      return fail(PA_ERANGE, "pair %lld (%lld -> %lld) outside [0, %lld)", (long long)i, (long long)s, (long long)d, (long long)NB);
+    src.insert(s);
+    if (!dst.insert(d).second) return fail(PA_EINVAL, "destination %lld repeated (pair %lld)", (long long)d, (long long)i);
+  }
+  for (int64_t d : dst)
+    if (src.count(d)) return fail(PA_EINVAL, "frame %lld is both a source and a destination", (long long)d);
+  return ok();
+}
+
+int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int num_chunks, int block_size, int64_t NB, int max_chunk_len,
+                              int max_context_len) {
+  if (num_chunks < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1) return fail(PA_EINVAL, "bad sizes");
+  if (num_chunks > 0 && (!block_tables || !query_start_loc || !context_lens))
+    return fail(PA_EINVAL, "null pointer argument");
+  if (num_chunks > 0 && query_start_loc[0] != 0) return fail(PA_EINVAL, "query_start_loc[0] = %d, must be 0", query_start_loc[0]);
+  const long long cap = std::min<long long>(max_context_len, (long long)max_blocks_per_seq * block_size);
+  for (int c = 0; c < num_chunks; ++c) {
+    const int C = query_start_loc[c + 1] - query_start_loc[c];
+    const int L = context_lens[c];
+    if (C < 0) return fail(PA_EINVAL, "query_start_loc decreases at %d", c);
+    if (C > max_chunk_len) return fail(PA_ERANGE, "chunk %d has %d rows > max_chunk_len %d", c, C, max_chunk_len);
+    if (L < 1 || L > cap) return fail(PA_ERANGE, "context_lens[%d] = %d outside [1, %lld]", c, L, cap);
+    if (C > L) return fail(PA_ERANGE, "chunk %d has %d rows but context length %d", c, C, L);
+    const int nblk = (L + block_size - 1) / block_size;
+    for (int i = 0; i < nblk; ++i) {
+      const int32_t f = block_tables[(size_t)c * max_blocks_per_seq + i];
+      if (f < 0 || f >= NB)
+        return fail(PA_ERANGE, "block_tables[%d][%d] = %d outside [0, %lld)", c, i, f, (long long)NB);
+    }
+  }
+  return ok();
+}
+
+}  // extern "C"

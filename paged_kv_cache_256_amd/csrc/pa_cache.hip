@@ -1,0 +1,119 @@
+// pa_cache.hip -- cache writes (reshape_and_cache) and frame copies (copy_blocks) for gfx950.
+//
+// reshape_and_cache follows the block-table mapping of codebumble.net ("The Block Table
+// Mapping Subsystem"): a token's slot names its frame (slot / block_size) and its offset in
+// the frame (slot % block_size).  Each workgroup stores one token: every KV head's D values
+// go to their places in the (frame, head) tile of the operand-order layout.  An fp8 cache
+// stores e4m3fn(fp32(x) / scale), rounded to nearest even with saturation.
+//
+// copy_blocks implements the copy half of copy-on-write (infoisland, section 2): a frame
+// shared by several sequences is duplicated before one of them writes into it.
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+template <int SRC, int KV, int D, int BS>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const void* __restrict__ k, const void* __restrict__ v, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, const int64_t* __restrict__ slots, long long NB, int Hkv,
+    float k_scale, float v_scale) {
+  constexpr int EB = KV == KF32 ? 4 : (KV == KBF16 ? 2 : 1);
+  constexpr int TILE = BS * D * EB;
+  const long long i = blockIdx.x;
+  const long long s = slots[i];
+  if (s < 0 || s >= NB * BS) return;
+  const long long f = s / BS;
+  const int o = (int)(s % BS);
+  for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
+    const int g = idx / D, d = idx % D;
+    const size_t src = ((size_t)i * Hkv + g) * D + d;
+    const size_t tile = ((size_t)f * Hkv + g) * TILE;
+    char* kd = k_cache + tile + k_tile_byte(o, d, D, EB);
+    char* vd = v_cache + tile + v_tile_byte(o, d, D, EB);
+    if constexpr (KV == KF32) {
+      *(uint32_t*)kd = ((const uint32_t*)k)[src];
+      *(uint32_t*)vd = ((const uint32_t*)v)[src];
+    } else if constexpr (KV == KBF16) {
+      *(uint16_t*)kd = ((const uint16_t*)k)[src];
+      *(uint16_t*)vd = ((const uint16_t*)v)[src];
+    } else {
+      float xk, xv;
+      if constexpr (SRC == KF32) {
+        xk = ((const float*)k)[src];
+        xv = ((const float*)v)[src];
+      } else {
+        xk = __uint_as_float((uint32_t)((const uint16_t*)k)[src] << 16);
+        xv = __uint_as_float((uint32_t)((const uint16_t*)v)[src] << 16);
+      }
+      *(uint8_t*)kd = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xk, k_scale));
+      *(uint8_t*)vd = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xv, v_scale));
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void copy_blocks_kernel(char* __restrict__ k_cache,
+                                                          char* __restrict__ v_cache,
+                                                          const int64_t* __restrict__ pairs,
+                                                          long long NB, long long frame_bytes) {
+  const long long p = blockIdx.x;
+  const long long src = pairs[2 * p], dst = pairs[2 * p + 1];
+  if (src < 0 || src >= NB || dst < 0 || dst >= NB) return;
+  char* base = blockIdx.y ? v_cache : k_cache;
+  const u32x4* s = (const u32x4*)(base + src * frame_bytes);
+  u32x4* d = (u32x4*)(base + dst * frame_bytes);
+  const long long n16 = frame_bytes / 16;
+  for (long long t = threadIdx.x; t < n16; t += blockDim.x) d[t] = s[t];
+}
+
+template <int SRC, int KV, int D, int BS>
+hipError_t launch_reshape_typed(const void* k, const void* v, void* kc, void* vc,
+                                const int64_t* slots, int64_t T, int64_t NB, int Hkv,
+                                float ks, float vs, hipStream_t stream) {
+  hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KV, D, BS>), dim3((unsigned)T), dim3(256), 0,
+                     stream, k, v, (char*)kc, (char*)vc, slots, (long long)NB, Hkv, ks, vs);
+  return hipGetLastError();
+}
+
+template <int SRC, int KV>
+hipError_t launch_reshape_kind(const void* k, const void* v, void* kc, void* vc,
+                               const int64_t* slots, int64_t T, int64_t NB, int Hkv, int D,
+                               int bs, float ks, float vs, hipStream_t s) {
+  if (D == 64 && bs == 16) return launch_reshape_typed<SRC, KV, 64, 16>(k, v, kc, vc, slots, T, NB, Hkv, ks, vs, s);
+  if (D == 64 && bs == 32) return launch_reshape_typed<SRC, KV, 64, 32>(k, v, kc, vc, slots, T, NB, Hkv, ks, vs, s);
+  if (D == 128 && bs == 16) return launch_reshape_typed<SRC, KV, 128, 16>(k, v, kc, vc, slots, T, NB, Hkv, ks, vs, s);
+  if (D == 128 && bs == 32) return launch_reshape_typed<SRC, KV, 128, 32>(k, v, kc, vc, slots, T, NB, Hkv, ks, vs, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int64_t T, int64_t NB, int Hkv, int D,
+                                    int bs, int src_dtype, int kv_dtype, float k_scale,
+                                    float v_scale, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (src_dtype == DT_F32 && kv_dtype == DT_F32)
+    return launch_reshape_kind<KF32, KF32>(k, v, k_cache, v_cache, slots, T, NB, Hkv, D, bs, k_scale, v_scale, stream);
+  if (src_dtype == DT_BF16 && kv_dtype == DT_BF16)
+    return launch_reshape_kind<KBF16, KBF16>(k, v, k_cache, v_cache, slots, T, NB, Hkv, D, bs, k_scale, v_scale, stream);
+  if (src_dtype == DT_BF16 && kv_dtype == DT_FP8)
+    return launch_reshape_kind<KBF16, KFP8>(k, v, k_cache, v_cache, slots, T, NB, Hkv, D, bs, k_scale, v_scale, stream);
+  if (src_dtype == DT_F32 && kv_dtype == DT_FP8)
+    return launch_reshape_kind<KF32, KFP8>(k, v, k_cache, v_cache, slots, T, NB, Hkv, D, bs, k_scale, v_scale, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int64_t N,
+                              int64_t NB, int64_t frame_bytes, hipStream_t stream) {
+  if (N == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)N, 2), dim3(256), 0, stream,
+                     (char*)k_cache, (char*)v_cache, pairs, (long long)NB,
+                     (long long)frame_bytes);
+  return hipGetLastError();
+}
+
+}  // namespace pa

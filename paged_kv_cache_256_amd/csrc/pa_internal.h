@@ -1,0 +1,67 @@
+// pa_internal.h -- host-side launchers behind the C ABI (no validation here; pa_api.cpp checks
+// every scalar argument before calling these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum DType { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
+
+struct DecodeParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* context_lens;
+  int B, Hq, Hkv, D, bs;
+  int64_t NB;
+  float scale;
+  int kv_dtype;  // DType; q/out are f32 for an f32 cache, bf16 otherwise
+  float k_scale, v_scale;
+  int max_context_len;
+  void* workspace;
+};
+
+struct PrefillParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  int num_chunks;
+  int64_t total_q;
+  int max_chunk_len, max_context_len;
+  int Hq, Hkv, D, bs;
+  int64_t NB;
+  float scale;
+  int kv_dtype;
+  float k_scale, v_scale;
+  void* workspace;
+};
+
+// Tokens of context one decode workgroup covers (the split-K partition size).
+int decode_partition_tokens(int bs, int kv_dtype);
+size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+size_t prefill_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
+                               int max_context_len, int Hq, int Hkv, int D, int kv_dtype);
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int64_t T, int64_t NB, int Hkv, int D,
+                                    int bs, int src_dtype, int kv_dtype, float k_scale,
+                                    float v_scale, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int64_t N,
+                              int64_t NB, int64_t frame_bytes, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,400 @@
+// pa_prefill.hip -- causal attention of prefill chunks over their paged context (gfx950).
+//
+// What is computed (bicarait.com, "Architectural Blueprint 3"; infoisland, section 5): a long
+// prompt is processed in chunks (512 tokens in the pages' example) that run in the same step
+// as decodes.  Row i of a chunk of C rows in a sequence of L tokens sits at position
+// L - C + i and attends keys 0 .. L - C + i through the sequence's block table.
+//
+// The work is a dense contraction, so it runs on the matrix cores:
+//  * A workgroup (4 wavefronts) owns TQ chunk rows x the G heads of one kv head: each
+//    wavefront holds NT tiles of 16 query rows (row = token x head, so GQA heads of one token
+//    share every K/V fragment) as the columns of S^T = K Q^T.
+//  * K/V tiles are staged through LDS, 32 keys per stage, double-buffered: all 256 threads
+//    fetch the next stage's tiles with contiguous 16-byte loads while the wavefronts compute
+//    on the current one, and every wavefront then reads the same tile from LDS, so one fetch
+//    from L2/HBM serves 4 x NT x 16 query rows.
+//  * Online softmax per query row (causal mask on the diagonal stages), O^T += V^T P^T with
+//    32-key 16x16x32 steps.
+//  * The context is split into KS-key ranges across workgroups so that a single chunk fills
+//    the GPU; rows covered by one range are written directly, the others as unnormalised
+//    partials merged by prefill_reduce_kernel (log-sum-exp rule).
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int kPWaves = 4;
+constexpr int kTargetWGs = 512; // workgroups the context split aims for
+
+// 16-row query tiles per wavefront (f32 operands take twice the registers).
+constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 2 : 4; }
+
+template <int KIND>
+struct PQ {
+  static constexpr int bytes = KIND == KF32 ? 4 : 2;
+};
+
+// One 32-key step of P*V for two 16-key groups gA, gB.
+template <int KIND, int D, int BS>
+struct PairPV {
+  using Ops = KvOps<KIND, D, BS>;
+  template <class V, class P>
+  __device__ static f32x4 run(f32x4 acc, V va, V vb, P pa_, P pb) {
+    if constexpr (KIND == KF32) {
+      return Ops::pv(Ops::pv(acc, va, pa_), vb, pb);
+    } else {
+      u32x4 a, b;
+      a[0] = va[0]; a[1] = va[1]; a[2] = vb[0]; a[3] = vb[1];
+      b[0] = pa_[0]; b[1] = pa_[1]; b[2] = pb[0]; b[3] = pb[1];
+      return mfma_x32_bf16(a, b, acc);
+    }
+  }
+};
+
+template <int KIND, int D, int BS, int NT>
+__global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
+    void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, int mbps, int Hq, int Hkv, int G,
+    long long NB, long long total_q, int nsplit, int KS, int max_ctx, float qk_scale,
+    float v_scale) {
+  using Ops = KvOps<KIND, D, BS>;
+  constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
+  constexpr int TILE = Ops::TILE;
+  constexpr int SF = 32 / BS;            // frames per 32-key stage
+  constexpr int NG = SF * KG;            // 16-key groups per stage (= 2)
+  constexpr int STAGE = SF * 2 * TILE;   // bytes: [frame][K,V][tile]
+  constexpr int PPT = STAGE / 16 / (kPWaves * 64);
+  static_assert(NG == 2, "a stage is two 16-key groups");
+  static_assert(PPT >= 1 && STAGE % (16 * kPWaves * 64) == 0, "stage must split over threads");
+  constexpr int QB = PQ<KIND>::bytes;
+
+  __shared__ __attribute__((aligned(16))) char smem[2][STAGE];
+
+  const int x = blockIdx.x, qt = blockIdx.y;
+  const int c = blockIdx.z / Hkv, g = blockIdx.z % Hkv;
+  const int w = uniform(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
+
+  const int r0 = qsl[c];
+  const int C = qsl[c + 1] - r0;
+  const int cap = min(max_ctx, mbps * BS);
+  const int L = min(context_lens[c], cap);
+  if (r0 < 0 || (long long)qsl[c + 1] > total_q || C <= 0 || C > L) return;
+  const int TQ = kPWaves * NT * 16 / G;
+  const int t0 = qt * TQ;
+  if (t0 >= C) return;
+  const int pos0 = L - C;
+  const int tq_end = min(t0 + TQ, C);
+  const int kbeg = x * KS;
+  const int kend = min(kbeg + KS, pos0 + tq_end);
+  if (kbeg >= kend) return;
+
+  // Query fragments and positions of this wavefront's NT tiles.
+  uint32_t qw[NT][QW];
+  int rpos[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int qrow = (w * NT + t) * 16 + n;
+    const int tok = t0 + qrow / G;
+    const bool ok = tok < C;
+    rpos[t] = ok ? pos0 + tok : -1;
+    const size_t row = (size_t)(r0 + (ok ? tok : 0)) * Hq + (size_t)g * G + qrow % G;
+    const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
+#pragma unroll
+    for (int i = 0; i < QW / 4; ++i) {
+      u32x4 v = src[i];
+      if (!ok) v = (u32x4){0u, 0u, 0u, 0u};
+      qw[t][4 * i] = v[0]; qw[t][4 * i + 1] = v[1]; qw[t][4 * i + 2] = v[2]; qw[t][4 * i + 3] = v[3];
+    }
+  }
+
+  float m[NT], lsum[NT];
+  f32x4 acc[NT][NC];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m[t] = -INFINITY;
+    lsum[t] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) acc[t][cc] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nst = (kend - kbeg + 31) / 32;
+  const size_t trow = (size_t)c * mbps;
+
+  // Fetch this thread's pieces of stage st (frames past kend or with invalid ids read zeros).
+  auto issue = [&](u32x4 (&buf)[PPT], int st) {
+    const int key0 = kbeg + 32 * st;
+    int fid[SF];
+#pragma unroll
+    for (int fl = 0; fl < SF; ++fl) {
+      const int fi = key0 / BS + fl;
+      int f = -1;
+      if (fi * BS < kend) f = block_tables[trow + fi];
+      fid[fl] = uniform((f >= 0 && (long long)f < NB) ? f : -1);
+    }
+#pragma unroll
+    for (int k = 0; k < PPT; ++k) {
+      const int p = threadIdx.x + k * kPWaves * 64;
+      const int fl = p / (2 * TILE / 16);
+      const int kind = (p / (TILE / 16)) & 1;
+      const int within = p % (TILE / 16);
+      int f = fid[0];
+#pragma unroll
+      for (int z = 1; z < SF; ++z)
+        if (fl == z) f = fid[z];
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+      if (f >= 0) {
+        const char* base = kind ? v_cache : k_cache;
+        v = *((const u32x4*)(base + ((size_t)f * Hkv + g) * TILE) + within);
+      }
+      buf[k] = v;
+    }
+  };
+  auto stash = [&](const u32x4 (&buf)[PPT], int slot) {
+#pragma unroll
+    for (int k = 0; k < PPT; ++k)
+      *((u32x4*)smem[slot] + threadIdx.x + k * kPWaves * 64) = buf[k];
+  };
+
+  auto compute = [&](int st) {
+    const char* sb = smem[st & 1];
+    const int key0 = kbeg + 32 * st;
+    f32x4 s[NT][NG];
+#pragma unroll
+    for (int fl = 0; fl < SF; ++fl) {
+      u32x4 kt[NL];
+#pragma unroll
+      for (int r = 0; r < NL; ++r) kt[r] = *((const u32x4*)(sb + (2 * fl) * TILE + r * 1024) + lane);
+#pragma unroll
+      for (int h = 0; h < KG; ++h) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int sl = 0; sl < NS; ++sl) a = Ops::qk(a, Ops::kop(kt, h, sl), Ops::qop(qw[t], sl));
+          s[t][fl * KG + h] = a;
+        }
+      }
+    }
+    // mask, online softmax update per query row
+    typename Ops::PFrag pf[NT][NG];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const int key = key0 + 16 * gi + 4 * j + ii;
+          const float v = (key < kend && key <= rpos[t]) ? s[t][gi][ii] * qk_scale : -INFINITY;
+          s[t][gi][ii] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = wave_max_over_j(mx);
+      const float mnew = fmaxf(m[t], mx);
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m[t] - msafe);
+      m[t] = mnew;
+      lsum[t] *= alpha;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        f32x4 p;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(s[t][gi][ii] - msafe);
+        pf[t][gi] = Ops::pfrag(p, lsum[t]);
+      }
+    }
+    // P * V
+    u32x4 vt[SF][NL];
+#pragma unroll
+    for (int fl = 0; fl < SF; ++fl)
+#pragma unroll
+      for (int r = 0; r < NL; ++r) vt[fl][r] = *((const u32x4*)(sb + (2 * fl + 1) * TILE + r * 1024) + lane);
+    if (key0 + 32 > kend) {
+      // keys past the range end may be unwritten slots: clear their values
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[gi / KG], gi % KG, cc, keep);
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
+      const auto va = Ops::vop(vt[0], 0, cc);
+      const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][cc] = PairPV<KIND, D, BS>::run(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
+    }
+  };
+
+  u32x4 pre[PPT];
+  issue(pre, 0);
+  stash(pre, 0);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) issue(pre, st + 1);
+    compute(st);
+    if (st + 1 < nst) stash(pre, (st + 1) & 1);
+    __syncthreads();
+  }
+
+  // Results: direct output for rows covered by a single key range, partials otherwise.
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float lrow = wave_sum_over_j(lsum[t]);
+    if (rpos[t] < kbeg) continue;  // no key of this range is visible to the row
+    const int qrow = (w * NT + t) * 16 + n;
+    const size_t r = (size_t)r0 + (rpos[t] - pos0);
+    const size_t h = (size_t)g * G + qrow % G;
+    const int nsp = min(nsplit, rpos[t] / KS + 1);
+    if (nsp == 1) {
+      const float inv = v_scale / lrow;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const size_t o = (r * Hq + h) * D + 16 * cc + 4 * j;
+        if constexpr (KIND == KF32) {
+          *(f32x4*)((float*)out + o) = acc[t][cc] * inv;
+        } else {
+          u32x2 pk;
+          pk[0] = pack_bf16x2(acc[t][cc][0] * inv, acc[t][cc][1] * inv);
+          pk[1] = pack_bf16x2(acc[t][cc][2] * inv, acc[t][cc][3] * inv);
+          *(u32x2*)((__bf16*)out + o) = pk;
+        }
+      }
+    } else {
+      const size_t pi = (r * Hq + h) * nsplit + x;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) *(f32x4*)(ws_o + pi * D + 16 * cc + 4 * j) = acc[t][cc];
+      if (j == 0) {
+        ws_ml[2 * pi] = m[t];
+        ws_ml[2 * pi + 1] = lrow;
+      }
+    }
+  }
+}
+
+template <int KIND>
+__global__ __launch_bounds__(128) void prefill_reduce_kernel(
+    void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int num_chunks,
+    int Hq, int D, int nsplit, int KS, int cap, float v_scale) {
+  const long long r = blockIdx.x;
+  const int h = blockIdx.y;
+  int lo = 0, hi = num_chunks - 1;  // last chunk c with qsl[c] <= r
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (qsl[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  const int c = lo;
+  const int C = qsl[c + 1] - qsl[c];
+  const int L = min(context_lens[c], cap);
+  if (r < qsl[c] || r >= qsl[c + 1] || C <= 0 || C > L) return;
+  const int pos = L - C + (int)(r - qsl[c]);
+  const int nsp = min(nsplit, pos / KS + 1);
+  if (nsp <= 1) return;
+  const size_t base = ((size_t)r * Hq + h) * nsplit;
+  float M = -INFINITY;
+  for (int p = 0; p < nsp; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float num = 0.f, den = 0.f;
+    for (int p = 0; p < nsp; ++p) {
+      const float mp = ws_ml[2 * (base + p)];
+      if (mp == -INFINITY) continue;
+      const float e = __builtin_amdgcn_exp2f(mp - M);
+      num += e * ws_o[(base + p) * D + d];
+      den += e * ws_ml[2 * (base + p) + 1];
+    }
+    const float o = num / den * v_scale;
+    if constexpr (KIND == KF32) {
+      ((float*)out)[((size_t)r * Hq + h) * D + d] = o;
+    } else {
+      ((__bf16*)out)[((size_t)r * Hq + h) * D + d] = (__bf16)o;
+    }
+  }
+}
+
+struct Split {
+  int nsplit, KS;
+};
+
+Split choose_split(int num_chunks, int max_chunk_len, int max_ctx, int Hq, int Hkv, int kind) {
+  const int G = Hq / Hkv;
+  const int TQ = kPWaves * tiles_per_wave(kind) * 16 / G;
+  const long long tiles = (long long)num_chunks * ((max_chunk_len + TQ - 1) / TQ) * Hkv;
+  int want = (int)((kTargetWGs + tiles - 1) / (tiles > 0 ? tiles : 1));
+  const int most = (max_ctx + 255) / 256;
+  if (want > most) want = most;
+  if (want < 1) want = 1;
+  int KS = (max_ctx + want - 1) / want;
+  KS = ((KS + 63) / 64) * 64;
+  if (KS < 64) KS = 64;
+  return Split{(max_ctx + KS - 1) / KS, KS};
+}
+
+template <int KIND, int D, int BS>
+hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
+  constexpr int NT = tiles_per_wave(KIND);
+  const Split sp = choose_split(p.num_chunks, p.max_chunk_len, p.max_context_len, p.Hq, p.Hkv, KIND);
+  const int G = p.Hq / p.Hkv;
+  const int TQ = kPWaves * NT * 16 / G;
+  float* ws_ml = (float*)p.workspace;
+  float* ws_o = ws_ml ? ws_ml + (size_t)2 * p.total_q * p.Hq * sp.nsplit : nullptr;
+  const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
+  const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
+  dim3 grid(sp.nsplit, (p.max_chunk_len + TQ - 1) / TQ, p.num_chunks * p.Hkv);
+  hipLaunchKernelGGL((prefill_chunk_kernel<KIND, D, BS, NT>), grid, dim3(kPWaves * 64), 0,
+                     stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
+                     p.block_tables, p.query_start_loc, p.context_lens, ws_ml, ws_o,
+                     p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB,
+                     (long long)p.total_q, sp.nsplit, sp.KS, p.max_context_len, qk_scale, v_scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp.nsplit <= 1) return e;
+  const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
+                                                                 : p.max_blocks_per_seq * BS;
+  hipLaunchKernelGGL((prefill_reduce_kernel<KIND>), dim3((unsigned)p.total_q, p.Hq), dim3(D), 0,
+                     stream, p.out, ws_ml, ws_o, p.query_start_loc, p.context_lens,
+                     p.num_chunks, p.Hq, D, sp.nsplit, sp.KS, cap, v_scale);
+  return hipGetLastError();
+}
+
+template <int KIND>
+hipError_t launch_prefill_kind(const PrefillParams& p, hipStream_t s) {
+  if (p.D == 64 && p.bs == 16) return launch_prefill_typed<KIND, 64, 16>(p, s);
+  if (p.D == 64 && p.bs == 32) return launch_prefill_typed<KIND, 64, 32>(p, s);
+  if (p.D == 128 && p.bs == 16) return launch_prefill_typed<KIND, 128, 16>(p, s);
+  if constexpr (KIND != KF32) {
+    if (p.D == 128 && p.bs == 32) return launch_prefill_typed<KIND, 128, 32>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
+                               int max_context_len, int Hq, int Hkv, int D, int kv_dtype) {
+  const int kind = kv_dtype == DT_F32 ? KF32 : (kv_dtype == DT_BF16 ? KBF16 : KFP8);
+  const Split sp = choose_split(num_chunks, max_chunk_len, max_context_len, Hq, Hkv, kind);
+  if (sp.nsplit <= 1) return 0;
+  return (size_t)total_q * Hq * sp.nsplit * (2 + (size_t)D) * sizeof(float);
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  if (p.num_chunks == 0 || p.total_q == 0) return hipSuccess;
+  switch (p.kv_dtype) {
+    case DT_F32: return launch_prefill_kind<KF32>(p, stream);
+    case DT_BF16: return launch_prefill_kind<KBF16>(p, stream);
+    case DT_FP8: return launch_prefill_kind<KFP8>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pa
