@@ -1,0 +1,252 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+Default workload: the Llama-3-70B-shaped decode layer (256 sequences, 64 query heads, 8 KV
+heads, head_dim 128, bf16, 16-token blocks, context lengths log-uniform in [128, 8192] over a
+scattered pool).  One step = pa_reshape_and_cache of the step's 256 new tokens + pa_decode
+(plan, stream and reduce kernels), on inputs resident in HBM.  Before every timed step a 512 MiB
+buffer is read so the KV cache does not sit in L2 / the MALL from the previous step (a decode
+layer's KV is evicted by the other layers of a model in practice); the eviction is a read so that
+no dirty lines are written back inside the timed region.
+
+Prints ONE JSON line.  `value` is the KV GB/s of the whole step (algorithmic KV bytes / step
+time); seqs/s per layer, the roofline of the decode kernels and the CPU oracle's rate on a
+bounded sample are reported beside it.  --config N benches another of the five workloads
+(same fields); --gpus N>1 is refused (single-GPU build).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "paged-attn decode KV GB/s (% of HBM peak) + seqs/s, 70B-shape layer, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def chunk_flops(case) -> int:
+    """4 * D * Hq * sum_i (pos_i + 1): QK^T and P.V over the causal key ranges, 2 FLOP per MAC."""
+    ch = case.chunk
+    total = 0
+    for c in range(ch.num_chunks):
+        C = int(ch.query_start_loc[c + 1] - ch.query_start_loc[c])
+        L = int(ch.context_lens[c])
+        pos = np.arange(L - C, L, dtype=np.int64)
+        total += int((pos + 1).sum())
+    return 4 * case.D * case.Hq * total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_256_amd as pa
+    import workloads
+    from tests.gpu_harness import GpuStep
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    case = workloads.make(args.config)
+    log(f"[bench] generated config {args.config} ({case.name}) in {time.time() - t0:.1f}s")
+    g = GpuStep(case, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] caches filled on the GPU ({case.NB} frames)")
+
+    flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.float32, device=dev)
+
+    def one_step(ev):
+        ev[0].record()
+        if g.pairs is not None:
+            pa.copy_blocks(g.kc, g.vc, g.pairs, block_size=case.bs, kv_dtype=case.kv_dtype)
+        pa.reshape_and_cache(g.new_k, g.new_v, g.kc, g.vc, g.new_slots, block_size=case.bs,
+                             kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
+        ev[1].record()
+        if case.chunk is not None:
+            g.prefill()
+        ev[2].record()
+        if case.B:
+            g.decode(workspace=ws)
+        ev[3].record()
+
+    ws = None
+    if case.B:
+        need = pa.decode_workspace_bytes(case.B, case.Hq, case.D, case.bs, case.kv_dtype,
+                                         case.max_context_len)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    for _ in range(args.warmup):
+        if flush is not None:
+            flush.sum()
+        one_step(warm)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.sum()
+        one_step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    write_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    chunk_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    ms = float(step_ms.mean())
+
+    kv_bytes = case.decode_kv_bytes() if case.B else 0
+    qo_bytes = 2 * case.B * case.Hq * case.D * (4 if case.q_dtype == "f32" else 2)
+    value = kv_bytes / (ms * 1e-3) / 1e9 if case.B else 0.0
+    seqs_per_s = case.B / (ms * 1e-3)
+    dec_avg = float(dec_ms.mean())
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9 if case.B else 0.0
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "decode_plan_kernel + decode_stream_kernel + decode_reduce_kernel (one pa_decode call)",
+                "avg_us": round(dec_avg * 1e3, 2),
+                "algorithmic_bytes_per_launch": kv_bytes}
+    extra = {"write_us": round(float(write_ms.mean()) * 1e3, 2),
+             "decode_us": round(dec_avg * 1e3, 2),
+             "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
+                                   round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
+             "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None}
+    if case.chunk is not None:
+        fl = chunk_flops(case)
+        cavg = float(chunk_ms.mean())
+        extra["chunk_us"] = round(cavg * 1e3, 2)
+        extra["chunk_tflops"] = round(fl / (cavg * 1e-3) / 1e12, 2)
+        extra["chunk_frac_of_mfma_bf16_peak"] = round(fl / (cavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        extra["chunk_flop"] = fl
+        if not case.B:
+            roofline = {"bound": "mfma", "achieved": extra["chunk_tflops"],
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": extra["chunk_frac_of_mfma_bf16_peak"], "traffic": None,
+                        "kernel": "prefill_chunk_kernel (+ reduce)", "avg_us": extra["chunk_us"]}
+    log(f"[bench] step {ms * 1e3:.1f} us  decode {dec_avg * 1e3:.1f} us  -> {value:.0f} GB/s step, "
+        f"{achieved:.0f} GB/s decode ({achieved / HBM_PEAK_GBS * 100:.1f}% of 8 TB/s)")
+
+    cpu = None
+    if not args.no_cpu_baseline and case.B:
+        cpu = cpu_baseline(case, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "bf16 q / fp8-e4m3 kv"}[case.kv_dtype],
+        "data": "synthetic (seeded, shapes of the named layer; no weights or datasets)",
+        "config": {
+            "workload": case.name,
+            "cfg": args.config,
+            "batch": case.B,
+            "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
+            "block_size": case.bs, "kv_dtype": case.kv_dtype,
+            "context_tokens": int(case.context_lens.sum()) if case.B else 0,
+            "kv_bytes_per_step": kv_bytes,
+            "q_out_bytes_per_step": qo_bytes,
+            "seqs_per_s_per_layer": round(seqs_per_s, 1),
+            "kv_frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+            **extra,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload's sequences: the
+    step's cache writes for those sequences and their decode.  Rate on the same KV-byte
+    numerator as the GPU line."""
+    import oracle
+    from tests.gpu_harness import OracleStep
+
+    t0 = time.time()
+    o = OracleStep(case)
+    log(f"[bench] oracle caches built in {time.time() - t0:.1f}s")
+    rng = np.random.default_rng(0)
+    order = rng.permutation(case.B)
+    # calibrate on one sequence, then take as many as fit the budget
+    probe = [int(order[0])]
+    tp = time.perf_counter()
+    o.decode(probe)
+    per_token = (time.perf_counter() - tp) / max(1, int(case.context_lens[probe[0]]))
+    pick, tokens = [], 0
+    for b in order:
+        L = int(case.context_lens[b])
+        if pick and (tokens + L) * per_token > budget_s:
+            break
+        pick.append(int(b))
+        tokens += L
+    kw = dict(bs=case.bs, src_dtype=case.src_dtype, kv_dtype=case.kv_dtype,
+              k_scale=case.k_scale, v_scale=case.v_scale)
+    tstart = time.perf_counter()
+    oracle.reshape_and_cache(o.kc, o.vc, case.new_k[pick], case.new_v[pick], case.new_slots[pick], **kw)
+    o.decode(pick)
+    dt = time.perf_counter() - tstart
+    kv = case.decode_kv_bytes(np.array(pick))
+    return {"value": round(kv / dt / 1e9, 4), "unit": "GB/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{len(pick)} of {case.B} sequences ({tokens} context tokens): their "
+                      f"cache writes + fp64 decode, {dt:.1f}s",
+            "seconds": round(dt, 2), "seqs_per_s": round(len(pick) / dt, 3),
+            "host_cpu": cpu_model(), "host_logical_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -154,6 +154,14 @@ struct KvOps<KBF16, D, BS> {
     return pp;
   }
   __device__ static f32x4 pv(f32x4 acc, u32x2 v, PFrag p) { return mfma_x16_bf16(v, p, acc); }
+  // Two 16-key groups in one 16x16x32 step: elements 0-3 of each lane are group a's keys,
+  // elements 4-7 group b's, identically in the V^T and P^T fragments.
+  __device__ static f32x4 pv2(f32x4 acc, u32x2 va, u32x2 vb, PFrag pa, PFrag pb) {
+    u32x4 a, b;
+    a[0] = va[0]; a[1] = va[1]; a[2] = vb[0]; a[3] = vb[1];
+    b[0] = pa[0]; b[1] = pa[1]; b[2] = pb[0]; b[3] = pb[1];
+    return mfma_x32_bf16(a, b, acc);
+  }
   __device__ static void zero_quad(u32x4* t, int h, int c, int keep) {
     // zero the elements for keys 4j+i with i >= keep of quad (h, c)
     const int u = h * NC + c;
@@ -198,6 +206,9 @@ struct KvOps<KFP8, D, BS> {
   typedef u32x2 PFrag;
   __device__ static PFrag pfrag(f32x4 p, float& lsum) { return KvOps<KBF16, D, BS>::pfrag(p, lsum); }
   __device__ static f32x4 pv(f32x4 acc, u32x2 v, PFrag p) { return mfma_x16_bf16(v, p, acc); }
+  __device__ static f32x4 pv2(f32x4 acc, u32x2 va, u32x2 vb, PFrag pa, PFrag pb) {
+    return KvOps<KBF16, D, BS>::pv2(acc, va, vb, pa, pb);
+  }
   __device__ static void zero_quad(u32x4* t, int h, int c, int keep) {
     const int u = h * NC + c;
     const uint32_t m = keep >= 4 ? 0xffffffffu : ((1u << (8 * keep)) - 1u);
@@ -231,6 +242,9 @@ struct KvOps<KF32, D, BS> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc = mfma_x4_f32(__uint_as_float(v[i]), p[i], acc);
     return acc;
+  }
+  __device__ static f32x4 pv2(f32x4 acc, u32x4 va, u32x4 vb, PFrag pa, PFrag pb) {
+    return pv(pv(acc, va, pa), vb, pb);
   }
   __device__ static void zero_quad(u32x4* t, int h, int c, int keep) {
     u32x4& x = t[h * NC + c];

@@ -47,8 +47,9 @@ struct PrefillParams {
   void* workspace;
 };
 
-// Tokens of context one decode workgroup covers (the split-K partition size).
-int decode_partition_tokens(int bs, int kv_dtype);
+// Compute units of the current device (cached per device; 256 when no device is visible).
+int device_compute_units();
+
 size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 

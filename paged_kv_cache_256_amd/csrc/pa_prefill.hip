@@ -37,23 +37,6 @@ struct PQ {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// One 32-key step of P*V for two 16-key groups gA, gB.
-template <int KIND, int D, int BS>
-struct PairPV {
-  using Ops = KvOps<KIND, D, BS>;
-  template <class V, class P>
-  __device__ static f32x4 run(f32x4 acc, V va, V vb, P pa_, P pb) {
-    if constexpr (KIND == KF32) {
-      return Ops::pv(Ops::pv(acc, va, pa_), vb, pb);
-    } else {
-      u32x4 a, b;
-      a[0] = va[0]; a[1] = va[1]; a[2] = vb[0]; a[3] = vb[1];
-      b[0] = pa_[0]; b[1] = pa_[1]; b[2] = pb[0]; b[3] = pb[1];
-      return mfma_x32_bf16(a, b, acc);
-    }
-  }
-};
-
 template <int KIND, int D, int BS, int NT>
 __global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
@@ -232,7 +215,7 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
       const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
 #pragma unroll
       for (int t = 0; t < NT; ++t)
-        acc[t][cc] = PairPV<KIND, D, BS>::run(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
+        acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
     }
   };
 
