@@ -69,6 +69,76 @@ def chunk_flops(case) -> int:
     return 4 * case.D * case.Hq * total
 
 
+class DeviceState:
+    """A workload's device buffers: the KV caches (filled once over every pool slot), the
+    step's inputs, and preallocated outputs and workspaces, so a step allocates nothing."""
+
+    def __init__(self, case, dev):
+        import torch
+
+        import paged_kv_cache_256_amd as pa
+
+        self.c = c = case
+        self.pa = pa
+
+        def dv(a, kind):
+            a = np.ascontiguousarray(a)
+            if kind == "bf16":
+                return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(a).to(dev)
+
+        s = c.src_dtype
+        self.kc, self.vc = pa.new_kv_cache(c.NB, c.Hkv, c.bs, c.D, c.kv_dtype, device=dev)
+        pk, pv = dv(c.pool_k, s), dv(c.pool_v, s)
+        slots = torch.arange(c.NB * c.bs, dtype=torch.int64, device=dev)
+        pa.reshape_and_cache(pk, pv, self.kc, self.vc, slots, block_size=c.bs,
+                             kv_dtype=c.kv_dtype, k_scale=c.k_scale, v_scale=c.v_scale)
+        del pk, pv, slots
+        self.new_k, self.new_v = dv(c.new_k, s), dv(c.new_v, s)
+        self.new_slots = dv(c.new_slots, "i64")
+        self.pairs = dv(c.copy_pairs, "i64") if len(c.copy_pairs) else None
+        if c.B:
+            self.q = dv(c.q, c.q_dtype)
+            self.tables = dv(c.block_tables, "i32")
+            self.lens = dv(c.context_lens, "i32")
+            self.out = torch.empty_like(self.q)
+            need = pa.decode_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype, c.max_context_len)
+            self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        if c.chunk is not None:
+            ch = c.chunk
+            self.cq = dv(ch.q, c.q_dtype)
+            self.ctables = dv(ch.block_tables, "i32")
+            self.cqsl = dv(ch.query_start_loc, "i32")
+            self.clens = dv(ch.context_lens, "i32")
+            self.cout = torch.empty_like(self.cq)
+            need = pa.prefill_chunk_workspace_bytes(
+                ch.num_chunks, self.cq.shape[0], ch.max_chunk_len, ch.max_context_len, c.Hq,
+                c.Hkv, c.D, c.bs, c.kv_dtype)
+            self.cws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def write(self):
+        c, pa = self.c, self.pa
+        if self.pairs is not None:
+            pa.copy_blocks(self.kc, self.vc, self.pairs, block_size=c.bs, kv_dtype=c.kv_dtype)
+        pa.reshape_and_cache(self.new_k, self.new_v, self.kc, self.vc, self.new_slots,
+                             block_size=c.bs, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
+                             v_scale=c.v_scale)
+
+    def prefill(self):
+        c, ch = self.c, self.c.chunk
+        self.pa.prefill_chunk(self.cq, self.kc, self.vc, self.ctables, self.cqsl, self.clens,
+                              block_size=c.bs, scale=c.scale, kv_dtype=c.kv_dtype,
+                              max_chunk_len=ch.max_chunk_len, max_context_len=ch.max_context_len,
+                              k_scale=c.k_scale, v_scale=c.v_scale, out=self.cout,
+                              workspace=self.cws)
+
+    def decode(self):
+        c = self.c
+        self.pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, block_size=c.bs,
+                       scale=c.scale, kv_dtype=c.kv_dtype, max_context_len=c.max_context_len,
+                       k_scale=c.k_scale, v_scale=c.v_scale, out=self.out, workspace=self.ws)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -79,6 +149,12 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture each phase of the step in a HIP graph and replay the graphs "
+                         "(default: launch every call from Python each step)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="run three plain device copies of this many MiB before the timed steps "
+                         "(a known-size reference for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
@@ -88,38 +164,58 @@ def main():
 
     import paged_kv_cache_256_amd as pa
     import workloads
-    from tests.gpu_harness import GpuStep
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
     case = workloads.make(args.config)
     log(f"[bench] generated config {args.config} ({case.name}) in {time.time() - t0:.1f}s")
-    g = GpuStep(case, dev)
+    st = DeviceState(case, dev)
     torch.cuda.synchronize()
     log(f"[bench] caches filled on the GPU ({case.NB} frames)")
 
     flush = None if args.no_flush else torch.ones(128 << 20, dtype=torch.float32, device=dev)
 
+    if args.calibration_copy_mib:
+        src = torch.ones(args.calibration_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # the three phases of a step; each is one call of the library
+    phases = [st.write, st.prefill if case.chunk is not None else None,
+              st.decode if case.B else None]
+    if args.graph:
+        # one HIP graph per phase: a step replays the three graphs, so no host time sits
+        # between the kernels of a phase
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in phases:
+                if f is not None:
+                    f()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for f in phases:
+            if f is None:
+                graphs.append(None)
+                continue
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                f()
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        phases = [gr.replay if gr is not None else None for gr in graphs]
+
     def one_step(ev):
         ev[0].record()
-        if g.pairs is not None:
-            pa.copy_blocks(g.kc, g.vc, g.pairs, block_size=case.bs, kv_dtype=case.kv_dtype)
-        pa.reshape_and_cache(g.new_k, g.new_v, g.kc, g.vc, g.new_slots, block_size=case.bs,
-                             kv_dtype=case.kv_dtype, k_scale=case.k_scale, v_scale=case.v_scale)
-        ev[1].record()
-        if case.chunk is not None:
-            g.prefill()
-        ev[2].record()
-        if case.B:
-            g.decode(workspace=ws)
-        ev[3].record()
-
-    ws = None
-    if case.B:
-        need = pa.decode_workspace_bytes(case.B, case.Hq, case.D, case.bs, case.kv_dtype,
-                                         case.max_context_len)
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        for i, f in enumerate(phases):
+            if f is not None:
+                f()
+            ev[i + 1].record()
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     warm = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
@@ -157,7 +253,8 @@ def main():
              "decode_us": round(dec_avg * 1e3, 2),
              "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
-             "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None}
+             "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None,
+             "launch": "hip graph per phase" if args.graph else "eager"}
     if case.chunk is not None:
         fl = chunk_flops(case)
         cavg = float(chunk_ms.mean())

@@ -48,27 +48,42 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, defines=(), lib_path: str | None = None,
+          obj_dir: str | None = None) -> str:
+    """Compile and link libpa.so.  `defines` (NAME=VALUE strings) and `lib_path` / `obj_dir`
+    build a variant of the library elsewhere (tuning experiments); the default build writes
+    paged_kv_cache_256_amd/libpa.so."""
     cc = hipcc()
-    os.makedirs(OUT_DIR, exist_ok=True)
+    out_dir = obj_dir or OUT_DIR
+    lib = lib_path or LIB
+    os.makedirs(out_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     objs, cmds = [], []
     for src in SOURCES:
-        obj = os.path.join(OUT_DIR, src.rsplit(".", 1)[0] + ".o")
+        obj = os.path.join(out_dir, src.rsplit(".", 1)[0] + ".o")
         objs.append(obj)
         path = os.path.join(CSRC, src)
         if src.endswith(".hip"):
-            cmds.append([cc, *COMMON, *DEVICE, "-c", path, "-o", obj])
+            cmds.append([cc, *COMMON, *dflags, *DEVICE, "-c", path, "-o", obj])
         else:
-            cmds.append([cc, *COMMON, "-c", path, "-o", obj])
+            cmds.append([cc, *COMMON, *dflags, "-c", path, "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
           "-Wl,-rpath,/opt/rocm/lib"], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-v", action="store_true")
+    ap.add_argument("-D", action="append", default=[], help="preprocessor define NAME=VALUE")
+    ap.add_argument("--lib", default=None, help="output library path (default: in the package)")
+    ap.add_argument("--objdir", default=None)
+    a = ap.parse_args()
+    print(build(verbose=a.v, defines=a.D, lib_path=a.lib, obj_dir=a.objdir))

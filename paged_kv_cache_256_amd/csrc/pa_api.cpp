@@ -11,7 +11,7 @@
 #include <unordered_set>
 #include <vector>
 
-#include "../../include/pa.h"
+#include "pa.h"
 #include "pa_internal.h"
 
 namespace {

@@ -6,15 +6,19 @@
 // frames.  The page's kernel gathers the frames during QK^T and lets different warps score
 // different blocks before a final normalised reduction ("CUDA Shared Memory Optimization").
 //
-// Work decomposition (split-K over the whole batch, stream style).  All (sequence b, kv head g,
-// logical block) frames of the batch form one sequence ordered by b, then g, then block:
-//     x(b, g, blk) = Hkv * cum[b] + g * nblk[b] + blk,   cum[b] = sum_{b' < b} nblk[b'],
-// and the W persistent wavefronts of the launch split it into W equal contiguous ranges.  Every
-// wavefront therefore streams the same number of tiles whatever the mix of context lengths (no
-// idle workgroups for short sequences, no tail of long ones).  A (b, g) run that lies inside one
-// wavefront's range is finished there and written to `out`; a run cut by a range boundary
-// leaves an unnormalised partial (max, sum, accumulator) in one of the two partial slots of each
-// wavefront it touches, and decode_reduce_kernel merges them with the log-sum-exp rule.
+// Work decomposition (split-K over the whole batch, stream style).  All (sequence b, kv head g)
+// runs of the batch are laid end to end, b-major, each costing u[b] = nblk[b] + R units: R units
+// for the fixed cost of starting a run (fetching its query, block ids and first tiles) and one
+// unit per 4 KiB-class frame:
+//     X(b, g) = Hkv * cum[b] + g * u[b],   cum[b] = sum_{b' < b} u[b'],
+// and the W persistent wavefronts of the launch split the units into W equal contiguous ranges.
+// Every wavefront therefore does the same work whatever the mix of context lengths: no idle
+// workgroups for short sequences, no tail of long ones, and no wavefront stuck with many more
+// run starts than the others.  A wavefront whose range starts inside a run's R units starts at
+// the run's first frame; one whose range ends inside them leaves the run to the next.  A run that
+// lies inside one wavefront's range is finished there and written to `out`; a run cut by a range
+// boundary leaves an unnormalised partial (max, sum, accumulator) in one of the two partial slots
+// of each wavefront it touches, and decode_reduce_kernel merges them with the log-sum-exp rule.
 //
 // Inside a wavefront: the frame ids of up to 64 blocks come in with one vector load (one id per
 // lane) and are broadcast with readlane; each step gathers F frames' K and V tiles straight into
@@ -38,6 +42,27 @@ constexpr int kWaves = 4;    // wavefronts per workgroup (each an independent wo
 constexpr int kWgPerCu = 2;  // persistent workgroups per compute unit (2 waves per SIMD)
 constexpr int kIds = 64;     // block ids fetched per vector load
 
+// Cost units of a (sequence, kv head) run of nblk frames: one per frame plus kRestart for the
+// run's fixed start-up cost (about two memory latencies, i.e. roughly two frames of a
+// wavefront's streaming time).
+#ifndef PA_DECODE_RESTART_UNITS
+#define PA_DECODE_RESTART_UNITS 2
+#endif
+constexpr int kRestart = PA_DECODE_RESTART_UNITS;
+__host__ __device__ inline int run_units(int nblk) { return nblk > 0 ? nblk + kRestart : 0; }
+
+// Tile loads bypass cache retention by default (each tile is read once per step).
+#ifndef PA_DECODE_NONTEMPORAL
+#define PA_DECODE_NONTEMPORAL 1
+#endif
+__device__ inline u32x4 load_tile16(const u32x4* p) {
+#if PA_DECODE_NONTEMPORAL
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
 // Frames per pipeline step: two when a tile is 4 KiB or less (double-buffered K+V of two frames
 // = 128 VGPRs), one for larger tiles.
 template <int KIND, int D, int BS>
@@ -48,60 +73,70 @@ struct QType {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// Plan: cum[0..B] (blocks before each sequence) and the start (b, g, blk) of every wavefront.
+// Plan: cum[0..B] (cost units before each sequence, per kv head) and the start (b, g, unit) of
+// every wavefront.  One workgroup; thread t owns the contiguous sequences [t*per, (t+1)*per).  A
+// block-wide scan of the per-thread unit counts gives every sequence its offset; then each
+// wavefront start a_w is located by a binary search over the 1024 per-thread offsets (in LDS) and
+// a walk over at most `per` sequences, one thread per wavefront.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ context_lens,
                                                            int32_t* __restrict__ plan, int B,
                                                            int Hkv, int BS, int cap, int W) {
   int32_t* cum = plan;
   int32_t* start = plan + B + 1;
-  __shared__ int32_t part[1024];
-  __shared__ int32_t carry;
-  const int t = threadIdx.x;
-  if (t == 0) carry = 0;
-  __syncthreads();
-  for (int base = 0; base < B; base += 1024) {
-    const int b = base + t;
-    int v = 0;
-    if (b < B) {
-      const int L = max(0, min(context_lens[b], cap));
-      v = (L + BS - 1) / BS;
-    }
-    part[t] = v;
-    __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int add = t >= off ? part[t - off] : 0;
-      __syncthreads();
-      part[t] += add;
-      __syncthreads();
-    }
-    if (b < B) cum[b] = carry + part[t] - v;
-    __syncthreads();
-    if (t == 1023) carry += part[1023];
-    __syncthreads();
+  __shared__ int32_t wsum[16];
+  __shared__ int32_t tex[1024];  // units before thread t's first sequence
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int per = (B + 1023) / 1024;
+  const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) mine += run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
+  int incl = mine;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
   }
-  if (t == 0) cum[B] = carry;
-  __threadfence();
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  const long long F = (long long)Hkv * carry;
+  int before = 0, total = 0;
+  for (int k = 0; k < 16; ++k) {
+    const int v = wsum[k];
+    if (k < wv) before += v;
+    total += v;
+  }
+  const int ex = before + incl - mine;
+  tex[t] = ex;
+  int c = ex;
+  for (int b = b0; b < b1; ++b) {
+    cum[b] = c;
+    c += run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
+  }
+  if (t == 1023) cum[B] = total;
+  __syncthreads();
+  const long long F = (long long)Hkv * total;
+  if (F <= 0) return;
+  const long long q = F / W;
+  const unsigned r = (unsigned)(F % W);
   for (int w = t; w < W; w += 1024) {
-    const long long a = F * w / W;
-    int b = 0, g = 0, blk = 0;
-    if (a < F) {
-      const long long ap = a / Hkv;
-      int lo = 0, hi = B - 1;  // last b with cum[b] <= ap: the sequence holding frame a
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cum[mid] <= ap) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      const int nb = cum[b + 1] - cum[b];
-      const long long r = a - (long long)Hkv * cum[b];
-      g = (int)(r / nb);
-      blk = (int)(r % nb);
+    const long long aw = q * w + (long long)(r * (unsigned)w / (unsigned)W);  // floor(F w / W)
+    const int ap = (int)(aw / Hkv);
+    int lo = 0, hi = 1023;  // last thread whose first offset is <= ap (it holds unit aw)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tex[mid] <= ap) lo = mid; else hi = mid - 1;
     }
+    int cc = tex[lo];
+    int b = min(B, lo * per);
+    const int bend = min(B, b + per);
+    int su = 0;
+    for (; b < bend; ++b) {
+      su = run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
+      if (ap < cc + su) break;
+      cc += su;
+    }
+    const int off = (int)(aw - (long long)Hkv * cc);
     start[3 * w] = b;
-    start[3 * w + 1] = g;
-    start[3 * w + 2] = blk;
+    start[3 * w + 1] = su > 0 ? off / su : 0;
+    start[3 * w + 2] = su > 0 ? off % su : 0;
   }
 }
 
@@ -129,7 +164,7 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
   const long long Ftot = (long long)Hkv * cum[B];
   const long long a = range_begin(Ftot, w, W), e = range_begin(Ftot, w + 1, W);
   if (a >= e) return;
-  int b = start[3 * w], g = start[3 * w + 1], blk = start[3 * w + 2];
+  int b = start[3 * w], g = start[3 * w + 1], u = start[3 * w + 2];  // u: unit within the run
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[NC];
@@ -154,9 +189,9 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
       const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
       const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
 #pragma unroll
-      for (int r = 0; r < NL; ++r) kt[f][r] = __builtin_nontemporal_load(kp + r * 64);
+      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16(kp + r * 64);
 #pragma unroll
-      for (int r = 0; r < NL; ++r) vt[f][r] = __builtin_nontemporal_load(vp + r * 64);
+      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16(vp + r * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -230,10 +265,14 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
   while (x < e && b < B) {
     L = max(0, min(context_lens[b], cap));
     const int nblk = (L + BS - 1) / BS;
-    const int n_here = (int)min((long long)(nblk - blk), e - x);
+    const int units = (int)min((long long)(run_units(nblk) - u), e - x);  // of this run, here
+    // frames of the run inside this wavefront's range (its first kRestart units hold none)
+    const int f0 = max(0, u - kRestart), f1 = min(nblk, u + units - kRestart);
+    const int n_here = f1 - f0;
     if (n_here > 0) {
-      const long long s0 = x - blk;  // first frame of this (b, g) run
-      const bool complete = blk == 0 && n_here == nblk;
+      const long long s0 = x - u;  // first unit of this (b, g) run
+      const bool complete = f0 == 0 && f1 == nblk;
+      const int blk = f0;
       // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G)
       {
         const bool qv = n < G;
@@ -297,8 +336,8 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
         }
       }
     }
-    x += n_here > 0 ? n_here : 0;
-    blk = 0;
+    x += units > 0 ? units : 0;
+    u = 0;
     if (++g == Hkv) {
       g = 0;
       ++b;
@@ -308,43 +347,89 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
 
 // Merge the partials of every (b, g) run that crosses a wavefront boundary:
 // out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, M = max_w m_w.
+// The wavefronts holding the run are w0..w1; wavefront w keeps it in slot 1 if the run began
+// after the start of w's range (then it is w's last run), else in slot 0.
 template <int KIND>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int B, int Hq, int Hkv, int G, int D, int W,
     float v_scale) {
-  const int g = blockIdx.x, b = blockIdx.y;
+  // One workgroup per (b, g); runs finished inside one stream wavefront exit at once.
+  constexpr int kPer = 8;   // outputs per thread: G * D <= 16 * 128 = 8 * 256
+  constexpr int kBatch = 4; // partials whose loads are issued together
+  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int32_t* cum = plan;
-  const long long F = (long long)Hkv * cum[B];
-  const int nblk = cum[b + 1] - cum[b];
-  if (nblk <= 0 || F <= 0) return;
-  const long long s0 = (long long)Hkv * cum[b] + (long long)g * nblk;
-  const long long s1 = s0 + nblk;
-  // wavefront holding frame x: the largest w with floor(F w / W) <= x
-  const int w0 = (int)(((s0 + 1) * W + F - 1) / F - 1);
-  const int w1 = (int)((s1 * W + F - 1) / F - 1);
+  const int c0 = cum[b], c1 = cum[b + 1], cB = cum[B];
+  const long long F = (long long)Hkv * cB;
+  const int su = c1 - c0;  // units of each kv head's run of sequence b
+  const int nblk = su - kRestart;
+  if (su <= 0 || nblk <= 0 || F <= 0) return;
+  const long long s0 = (long long)Hkv * c0 + (long long)g * su;  // first unit of the run
+  const long long x0 = s0 + kRestart, x1 = s0 + su - 1;           // its first and last frame
+  // wavefront holding unit x: the largest w with floor(F w / W) <= x
+  const int w0 = (int)(((x0 + 1) * W + F - 1) / F - 1);
+  const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
   if (w0 == w1) return;  // finished inside one wavefront
-  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
-    const int r = idx / D, d = idx % D;
-    float M = -INFINITY;
-    for (int w = w0; w <= w1; ++w) {
-      const long long aw = range_begin(F, w, W);
-      if (aw >= range_begin(F, w + 1, W)) continue;
-      M = fmaxf(M, ws_ml[2 * (((size_t)w * 2 + (s0 > aw ? 1 : 0)) * 16 + r)]);
+  const long long q = F / W;
+  const unsigned r = (unsigned)(F % W);
+  const int nout = G * D;
+  float M[kPer], num[kPer], den[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    M[k] = -INFINITY;
+    num[k] = 0.f;
+    den[k] = 0.f;
+  }
+  // partials in wavefront order (a fixed merge order: the result does not depend on timing),
+  // kBatch at a time with all their loads in flight together
+  for (int wb = w0; wb <= w1; wb += kBatch) {
+    int row0[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int w = wb + i;
+      row0[i] = -1;
+      if (w <= w1) {
+        const long long aw = q * w + (long long)(r * (unsigned)w / (unsigned)W);
+        const long long aw1 = q * (w + 1) + (long long)(r * (unsigned)(w + 1) / (unsigned)W);
+        if (aw < aw1) row0[i] = (w * 2 + (s0 > aw ? 1 : 0)) * 16;
+      }
     }
-    float num = 0.f, den = 0.f;
-    for (int w = w0; w <= w1; ++w) {
-      const long long aw = range_begin(F, w, W);
-      if (aw >= range_begin(F, w + 1, W)) continue;
-      const size_t row = ((size_t)w * 2 + (s0 > aw ? 1 : 0)) * 16 + r;
-      const float mw = ws_ml[2 * row];
-      if (mw == -INFINITY) continue;
-      const float sc = __builtin_amdgcn_exp2f(mw - M);
-      num += sc * ws_o[row * D + d];
-      den += sc * ws_ml[2 * row + 1];
-    }
-    const float o = num / den * v_scale;
-    const size_t oi = ((size_t)b * Hq + (size_t)g * G + r) * D + d;
+    float mw[kBatch][kPer], lw[kBatch][kPer], ow[kBatch][kPer];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        const int idx = t + 256 * k;
+        const int rr = idx / D;
+        const bool ok = row0[i] >= 0 && idx < nout;
+        const size_t prow = (size_t)(ok ? row0[i] + rr : 0);
+        mw[i][k] = ok ? ws_ml[2 * prow] : -INFINITY;
+        lw[i][k] = ok ? ws_ml[2 * prow + 1] : 0.f;
+        ow[i][k] = ok ? ws_o[prow * D + (idx - rr * D)] : 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+#pragma unroll
+      for (int k = 0; k < kPer; ++k) {
+        if (mw[i][k] == -INFINITY) continue;
+        if (mw[i][k] > M[k]) {
+          const float sc = __builtin_amdgcn_exp2f(M[k] - mw[i][k]);
+          num[k] *= sc;
+          den[k] *= sc;
+          M[k] = mw[i][k];
+        }
+        const float e = __builtin_amdgcn_exp2f(mw[i][k] - M[k]);
+        num[k] += e * ow[i][k];
+        den[k] += e * lw[i][k];
+      }
+  }
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int idx = t + 256 * k;
+    if (idx >= nout) break;
+    const int rr = idx / D, d = idx - rr * D;
+    const float o = num[k] / den[k] * v_scale;
+    const size_t oi = ((size_t)b * Hq + (size_t)g * G + rr) * D + d;
     if constexpr (KIND == KF32) {
       ((float*)out)[oi] = o;
     } else {

@@ -268,3 +268,75 @@ def test_one_token_and_identical_keys_closed_forms_on_gpu():
     for h in range(Hkv * G):
         assert np.abs(o[0, h] - mean[h // G]).max() < 4e-3
         np.testing.assert_array_equal(o[1, h], vrows[0, h // G].double().numpy())
+
+
+STREAM_CASES = [
+    # (name, Hq, Hkv, kv, bs, lengths): extremes of the batch-wide stream split
+    ("one-sequence-over-every-wavefront", 8, 1, "bf16", 16, [100000]),
+    ("thousands-of-tiny-sequences", 8, 2, "bf16", 16, "tiny"),
+    ("long-and-tiny-mix-fp8", 16, 2, "fp8", 32, [1, 2, 40000, 3, 17, 33]),
+]
+
+
+@pytest.mark.parametrize("name,Hq,Hkv,kv,bs,lens", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_decode_stream_split_extremes(name, Hq, Hkv, kv, bs, lens):
+    _say(f"stream case {name}")
+    if lens == "tiny":
+        lens = lambda rng: rng.integers(1, 41, size=3000)
+    c = workloads.decode_case(name, 7, Hq=Hq, Hkv=Hkv, D=128, bs=bs, lens=lens, kv_dtype=kv,
+                              std=0.7071, pool="scattered")
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_decode(g, o)
+
+
+def test_graph_replays_match_eager_bits():
+    """A step captured in a HIP graph (copies, cache writes, prefill chunk, decode) and replayed
+    several times, with eager work between the replays, gives the eager step's bits each time."""
+    _say("graph replay case")
+    c = workloads.fork_case("graph-fork", 11, prompts=3, branches=3, prompt_len=320, tail_lo=1,
+                            tail_hi=60, Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16")
+    g = GpuStep(c)
+    ch = workloads.chunk_case("graph-chunk", 12, Hq=16, Hkv=2, D=128, bs=16,
+                              chunks=[(33, 200), (70, 900)], decode_lens=[5, 400, 1200],
+                              kv_dtype="bf16", std=0.7071)
+    h = GpuStep(ch)
+    dev = g.dev
+    ws = torch.empty(pa.decode_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype,
+                                               c.max_context_len), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(g.q)
+    cout = torch.empty_like(h.cq)
+
+    def step():
+        g.write()
+        g.decode(out=out, workspace=ws)
+        h.write()
+        h.prefill()
+        cout.copy_(h.chunk_out)
+
+    step()
+    torch.cuda.synchronize()
+    want, cwant = out.clone(), cout.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        step()
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.zero_()
+        cout.zero_()
+        # eager work between the replays: another decode into a fresh buffer
+        g.decode()
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"decode, replay {r}"
+        assert torch.equal(cout.view(torch.int16), cwant.view(torch.int16)), f"prefill, replay {r}"
+    o = OracleStep(c)
+    err = np.abs(out_f64(out) - o.decode()).max()
+    assert err <= tolerance(c)

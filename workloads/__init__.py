@@ -14,6 +14,7 @@ from .cases import (  # noqa: F401
     make,
     decode_case,
     chunk_case,
+    fork_case,
     CONFIG_NAMES,
     POISON_K,
     POISON_V,
