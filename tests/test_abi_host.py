@@ -1,0 +1,249 @@
+"""The C ABI of libpa.so on the host: the library loads, exports every function include/pa.h
+declares, and rejects bad scalar arguments before it touches the GPU.  No kernel runs here:
+every call below fails (or returns early) in argument checking, and pointer arguments that
+are not null are never dereferenced on those paths.
+"""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_256_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+OK, EINVAL, ERANGE, ENOTSUP, EHIP, ENOSPC = 0, -1, -2, -3, -4, -5
+F32, BF16, FP8 = 0, 1, 2
+FAKE = ctypes.c_void_p(0x1000)  # a non-null pointer never dereferenced on these paths
+NULL = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(pa_\w+)\s*\(", text, flags=re.M)))
+
+
+def lib():
+    return pa.lib()
+
+
+def err():
+    return lib().pa_last_error().decode()
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for want in ("pa_reshape_and_cache", "pa_copy_blocks", "pa_decode", "pa_prefill_chunk",
+                 "pa_decode_workspace_bytes", "pa_prefill_chunk_workspace_bytes",
+                 "pa_last_error", "pa_build_info", "pa_validate_decode_indices",
+                 "pa_validate_slots", "pa_validate_copy_pairs", "pa_validate_chunk_indices"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    raw = ctypes.CDLL(pa.LIB_PATH)
+    names = declared_functions()
+    missing = [n for n in names if not hasattr(raw, n)]
+    assert not missing, f"declared in pa.h but not exported: {missing}"
+    assert set(names) == set(pa.EXPORTED), "binding signatures differ from the header"
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l and l.split()[-1].startswith("pa_")}
+    assert exported == set(names), f"exported pa_* symbols {sorted(exported ^ set(names))} differ"
+
+
+def test_build_info_names_the_architecture():
+    assert "gfx950" in pa.build_info()
+
+
+def test_package_import_fails_loudly_without_the_library(tmp_path):
+    pkg = tmp_path / "paged_kv_cache_256_amd"
+    shutil.copytree(os.path.join(ROOT, "paged_kv_cache_256_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "csrc", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import paged_kv_cache_256_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "no fallback" in r.stderr
+
+
+# ----------------------------------------------------------------------------- pa_decode
+
+
+def decode(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=8, cl=FAKE, B=4, Hq=8, Hkv=2, D=128,
+             bs=16, NB=64, scale=0.1, qd=BF16, kvd=BF16, ks=1.0, vs=1.0, mcl=128, ws=NULL, wsb=0)
+    a.update(kw)
+    return lib().pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"], a["cl"], a["B"],
+                           a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["qd"], a["kvd"],
+                           a["ks"], a["vs"], a["mcl"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(out=NULL), EINVAL, "null pointer"),
+    (dict(bt=NULL), EINVAL, "null pointer"),
+    (dict(B=-1), EINVAL, "bad sizes"),
+    (dict(NB=0), EINVAL, "bad sizes"),
+    (dict(B=70000), ENOTSUP, "batch"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(Hq=6, Hkv=2), ENOTSUP, "query heads per kv head"),
+    (dict(Hq=64, Hkv=2), ENOTSUP, "query heads per kv head"),
+    (dict(D=96), ENOTSUP, "head_dim"),
+    (dict(bs=8), ENOTSUP, "block_size"),
+    (dict(qd=F32, kvd=BF16), ENOTSUP, "dtype combination"),
+    (dict(qd=BF16, kvd=F32), ENOTSUP, "dtype combination"),
+    (dict(qd=F32, kvd=F32, D=128, bs=32), ENOTSUP, "f32 cache"),
+    (dict(qd=7), EINVAL, "unknown dtype"),
+    (dict(kvd=FP8, ks=0.0), EINVAL, "fp8 scales"),
+    (dict(kvd=FP8, vs=float("nan")), EINVAL, "fp8 scales"),
+    (dict(scale=float("inf")), EINVAL, "scale"),
+    (dict(mcl=0), EINVAL, "max_context_len"),
+])
+def test_decode_rejects_bad_arguments(kw, code, msg):
+    assert decode(**kw) == code
+    assert msg in err()
+
+
+def test_decode_empty_batch_is_a_no_op_and_clears_the_error():
+    assert decode(D=96) == ENOTSUP
+    assert decode(B=0, out=NULL, q=NULL, kc=NULL, vc=NULL, bt=NULL, cl=NULL) == OK
+    assert err() == ""
+
+
+def test_decode_checks_the_workspace_size():
+    need = lib().pa_decode_workspace_bytes(4, 8, 128, 16, BF16, 128)
+    assert need > 0
+    assert decode(ws=NULL, wsb=0) == ENOSPC
+    assert f"{need} bytes needed" in err()
+    assert decode(ws=FAKE, wsb=need - 1) == ENOSPC
+
+
+def test_decode_workspace_grows_with_the_batch_and_is_zero_for_bad_arguments():
+    f = lib().pa_decode_workspace_bytes
+    assert f(0, 8, 128, 16, BF16, 128) == 0
+    assert f(4, 8, 128, 16, BF16, 0) == 0
+    assert f(65535, 64, 128, 16, BF16, 8192) > f(4, 64, 128, 16, BF16, 8192)
+
+
+# ----------------------------------------------------------------------------- pa_prefill_chunk
+
+
+def prefill(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=8, qsl=FAKE, cl=FAKE, nc=2, tq=40,
+             mcl=32, mctx=128, Hq=8, Hkv=2, D=64, bs=16, NB=64, scale=0.1, qd=BF16, kvd=BF16,
+             ks=1.0, vs=1.0, ws=NULL, wsb=0)
+    a.update(kw)
+    return lib().pa_prefill_chunk(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"], a["qsl"],
+                                  a["cl"], a["nc"], a["tq"], a["mcl"], a["mctx"], a["Hq"], a["Hkv"],
+                                  a["D"], a["bs"], a["NB"], a["scale"], a["qd"], a["kvd"], a["ks"],
+                                  a["vs"], a["ws"], a["wsb"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qsl=NULL), EINVAL, "null pointer"),
+    (dict(nc=-1), EINVAL, "bad sizes"),
+    (dict(mcl=200, mctx=100), EINVAL, "max_chunk_len"),
+    (dict(mcl=0), EINVAL, "max_chunk_len"),
+    (dict(nc=40000, Hkv=2), ENOTSUP, "num_chunks * Hkv"),
+    (dict(tq=1 << 31), ENOTSUP, "total_q"),
+    (dict(D=256), ENOTSUP, "head_dim"),
+    (dict(qd=F32, kvd=FP8), ENOTSUP, "dtype combination"),
+    (dict(kvd=FP8, ks=-1.0), EINVAL, "fp8 scales"),
+])
+def test_prefill_rejects_bad_arguments(kw, code, msg):
+    assert prefill(**kw) == code
+    assert msg in err()
+
+
+def test_prefill_workspace_checks():
+    need = lib().pa_prefill_chunk_workspace_bytes(2, 40, 32, 128, 8, 2, 64, 16, BF16)
+    if need:
+        assert prefill(ws=NULL, wsb=0) == ENOSPC
+        assert prefill(ws=FAKE, wsb=need - 1) == ENOSPC
+    assert lib().pa_prefill_chunk_workspace_bytes(0, 40, 32, 128, 8, 2, 64, 16, BF16) == 0
+    assert lib().pa_prefill_chunk_workspace_bytes(2, 40, 32, 128, 8, 3, 64, 16, BF16) == 0
+    assert prefill(nc=0, out=NULL) == OK
+
+
+# ----------------------------------------------------------------------------- cache writes
+
+
+def test_reshape_and_cache_rejects_bad_arguments():
+    f = lib().pa_reshape_and_cache
+    args = lambda **k: [k.get("k", FAKE), FAKE, FAKE, FAKE, k.get("s", FAKE), k.get("T", 4),
+                        k.get("NB", 8), 2, k.get("D", 64), 16, k.get("src", BF16), k.get("kv", BF16),
+                        k.get("ks", 1.0), 1.0, NULL]
+    assert f(*args(k=NULL)) == EINVAL and "null pointer" in err()
+    assert f(*args(src=FP8, kv=FP8)) == EINVAL and "source dtype" in err()
+    assert f(*args(src=BF16, kv=F32)) == ENOTSUP
+    assert f(*args(src=F32, kv=BF16)) == ENOTSUP
+    assert f(*args(src=BF16, kv=FP8, ks=0.0)) == EINVAL
+    assert f(*args(T=-1)) == EINVAL
+    assert f(*args(T=1 << 31)) == ENOTSUP
+    assert f(*args(T=0, k=NULL, s=NULL)) == OK
+    assert f(*args(D=32)) == ENOTSUP
+
+
+def test_copy_blocks_rejects_bad_arguments():
+    f = lib().pa_copy_blocks
+    assert f(FAKE, FAKE, NULL, 3, 8, 2, 64, 16, BF16, NULL) == EINVAL
+    assert f(FAKE, FAKE, FAKE, -1, 8, 2, 64, 16, BF16, NULL) == EINVAL
+    assert f(FAKE, FAKE, FAKE, 3, 8, 2, 64, 8, BF16, NULL) == ENOTSUP
+    assert f(NULL, NULL, NULL, 0, 8, 2, 64, 16, BF16, NULL) == OK
+
+
+# ----------------------------------------------------------------------------- validators
+
+
+def test_validate_decode_indices():
+    bt = np.array([[0, 1, 2, 3], [4, 5, -1, -1]], np.int32)
+    pa.validate_decode_indices(bt, np.array([64, 20], np.int32), 16, 6, 64)
+    with pytest.raises(pa.PAError, match="ERANGE.*block_tables\\[1\\]\\[1\\]"):
+        pa.validate_decode_indices(bt, np.array([64, 20], np.int32), 16, 5, 64)
+    with pytest.raises(pa.PAError, match="context_lens\\[1\\] = 0"):
+        pa.validate_decode_indices(bt, np.array([64, 0], np.int32), 16, 6, 64)
+    with pytest.raises(pa.PAError, match="context_lens\\[0\\] = 65"):
+        pa.validate_decode_indices(bt, np.array([65, 1], np.int32), 16, 6, 128)
+    with pytest.raises(pa.PAError, match="context_lens\\[0\\] = 64"):
+        pa.validate_decode_indices(bt, np.array([64, 1], np.int32), 16, 6, 63)
+
+
+def test_validate_slots():
+    pa.validate_slots(np.array([0, 5, -1, -1, 127], np.int64), 8, 16)
+    with pytest.raises(pa.PAError, match="ERANGE"):
+        pa.validate_slots(np.array([0, 128], np.int64), 8, 16)
+    with pytest.raises(pa.PAError, match="written twice"):
+        pa.validate_slots(np.array([3, 4, 3], np.int64), 8, 16)
+
+
+def test_validate_copy_pairs():
+    pa.validate_copy_pairs(np.array([[0, 5], [0, 6], [1, 7]]), 8)
+    with pytest.raises(pa.PAError, match="repeated"):
+        pa.validate_copy_pairs(np.array([[0, 5], [1, 5]]), 8)
+    with pytest.raises(pa.PAError, match="both a source and a destination"):
+        pa.validate_copy_pairs(np.array([[0, 5], [5, 6]]), 8)
+    with pytest.raises(pa.PAError, match="ERANGE"):
+        pa.validate_copy_pairs(np.array([[0, 8]]), 8)
+
+
+def test_validate_chunk_indices():
+    bt = np.array([[0, 1, 2], [3, 4, 5]], np.int32)
+    qsl = np.array([0, 10, 30], np.int32)
+    pa.validate_chunk_indices(bt, qsl, np.array([40, 20], np.int32), 16, 6, 20, 48)
+    with pytest.raises(pa.PAError, match="rows but context length"):
+        pa.validate_chunk_indices(bt, qsl, np.array([40, 19], np.int32), 16, 6, 20, 48)
+    with pytest.raises(pa.PAError, match="max_chunk_len"):
+        pa.validate_chunk_indices(bt, qsl, np.array([40, 20], np.int32), 16, 6, 19, 48)
+    with pytest.raises(pa.PAError, match="must be 0"):
+        pa.validate_chunk_indices(bt, np.array([1, 10, 30], np.int32), np.array([40, 20], np.int32),
+                                  16, 6, 20, 48)
+    with pytest.raises(pa.PAError, match="decreases"):
+        pa.validate_chunk_indices(bt, np.array([0, 10, 5], np.int32), np.array([40, 20], np.int32),
+                                  16, 6, 20, 48)
