@@ -1,4 +1,5 @@
-// pa_decode.hip -- paged-attention decode for gfx950: plan, stream and reduce kernels.
+// pa_decode.hip -- paged-attention decode for gfx950: stream and reduce kernels (plus a plan
+// kernel for batches above 1024 sequences).
 //
 // What is computed (codebumble.net, "Architectural Anatomy" and its FAQ; bicarait.com,
 // "Architectural Blueprint 2"): for sequence b and query head h, exact softmax attention of
@@ -9,16 +10,19 @@
 // Work decomposition (split-K over the whole batch, stream style).  All (sequence b, kv head g)
 // runs of the batch are laid end to end, b-major, each costing u[b] = nblk[b] + R units: R units
 // for the fixed cost of starting a run (fetching its query, block ids and first tiles) and one
-// unit per 4 KiB-class frame:
+// unit per frame:
 //     X(b, g) = Hkv * cum[b] + g * u[b],   cum[b] = sum_{b' < b} u[b'],
-// and the W persistent wavefronts of the launch split the units into W equal contiguous ranges.
-// Every wavefront therefore does the same work whatever the mix of context lengths: no idle
-// workgroups for short sequences, no tail of long ones, and no wavefront stuck with many more
-// run starts than the others.  A wavefront whose range starts inside a run's R units starts at
-// the run's first frame; one whose range ends inside them leaves the run to the next.  A run that
-// lies inside one wavefront's range is finished there and written to `out`; a run cut by a range
-// boundary leaves an unnormalised partial (max, sum, accumulator) in one of the two partial slots
-// of each wavefront it touches, and decode_reduce_kernel merges them with the log-sum-exp rule.
+// and the W persistent wavefronts of the launch split the F = Hkv * cum[B] units into W equal
+// contiguous ranges [floor(F w / W), floor(F (w+1) / W)).  Every wavefront therefore does the same
+// work whatever the mix of context lengths: no idle workgroups for short sequences, no tail of
+// long ones, and no wavefront stuck with many more run starts than the others.  Each wavefront
+// finds where its range starts with a scan over the batch's lengths (done inside the wavefront
+// for up to 1024 sequences, by a one-workgroup plan kernel above that).  A wavefront whose range
+// starts inside a run's R units starts at the run's first frame; one whose range ends inside them
+// leaves the run to the next.  A run that lies inside one wavefront's range is finished there and
+// written to `out`; a run cut by range boundaries leaves an unnormalised partial (max, sum,
+// accumulator) in one of the two partial slots of each wavefront it touches, and the reduce
+// kernel merges them with the log-sum-exp rule.
 //
 // Inside a wavefront: the frame ids of up to 64 blocks come in with one vector load (one id per
 // lane) and are broadcast with readlane; each step gathers F frames' K and V tiles straight into
@@ -73,16 +77,75 @@ struct QType {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// Plan: cum[0..B] (cost units before each sequence, per kv head) and the start (b, g, unit) of
-// every wavefront.  One workgroup; thread t owns the contiguous sequences [t*per, (t+1)*per).  A
-// block-wide scan of the per-thread unit counts gives every sequence its offset; then each
-// wavefront start a_w is located by a binary search over the 1024 per-thread offsets (in LDS) and
-// a walk over at most `per` sequences, one thread per wavefront.
+// The plan of a launch: plan[0] = U, the cost units of one kv head summed over the batch (the
+// launch holds F = Hkv * U units), then from plan[4] one int4 per wavefront w: the run (b, g)
+// holding unit a_w = floor(F w / W), the unit u of that run at which a_w falls, and the run's
+// unit count su.
+
+// Start of wavefront w found inside the wavefront itself (batches of at most kInlinePlanMax
+// sequences): lane l sums the units of sequences [l*per, (l+1)*per), a wave-wide scan gives every
+// lane its offset, a ballot finds the lane holding unit a_w / Hkv and a walk over its (at most 16)
+// sequences finds the run.
+constexpr int kInlinePlanMax = 1024;
+
+struct Start {
+  int b, g, u, su;
+  long long F;
+};
+
+__device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int B, int Hkv, int BS,
+                                  int cap, int W, int w, int lane) {
+  constexpr int kPer = kInlinePlanMax / 64;
+  const int per = (B + 63) / 64;
+  int un[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int bb = lane * per + i;
+    const int L = (i < per && bb < B) ? max(0, min(context_lens[bb], cap)) : 0;
+    un[i] = run_units((L + BS - 1) / BS);
+    mine += un[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  const int U = __builtin_amdgcn_readlane(incl, 63);
+  const int ex = incl - mine;
+  Start st;
+  st.F = (long long)Hkv * U;
+  const long long aw = st.F * w / W;
+  const int ap = (int)(aw / Hkv);
+  // lanes whose first offset is <= ap form a prefix; the last of them holds unit ap
+  const int k = __popcll(__ballot(ex <= ap)) - 1;
+  int cc = __builtin_amdgcn_readlane(ex, k);
+  int bb = k * per, su = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i < per && bb < B) {
+      su = __builtin_amdgcn_readlane(un[i], k);
+      if (ap < cc + su) break;
+      cc += su;
+      ++bb;
+    }
+  }
+  const int off = (int)(aw - (long long)Hkv * cc);
+  st.b = bb;
+  st.g = su > 0 ? off / su : 0;
+  st.u = su > 0 ? off % su : 0;
+  st.su = su;
+  return st;
+}
+
+// The same plan for any batch size, in one workgroup: thread t owns the contiguous sequences
+// [t*per, (t+1)*per); a block-wide scan of the per-thread unit counts gives every thread its
+// offset; each wavefront start is then located by a binary search over the 1024 per-thread
+// offsets (in LDS) and a walk over at most `per` sequences, one thread per wavefront.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ context_lens,
                                                            int32_t* __restrict__ plan, int B,
                                                            int Hkv, int BS, int cap, int W) {
-  int32_t* cum = plan;
-  int32_t* start = plan + B + 1;
   __shared__ int32_t wsum[16];
   __shared__ int32_t tex[1024];  // units before thread t's first sequence
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -103,22 +166,15 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
     if (k < wv) before += v;
     total += v;
   }
-  const int ex = before + incl - mine;
-  tex[t] = ex;
-  int c = ex;
-  for (int b = b0; b < b1; ++b) {
-    cum[b] = c;
-    c += run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
-  }
-  if (t == 1023) cum[B] = total;
+  tex[t] = before + incl - mine;
+  if (t == 0) plan[0] = total;
   __syncthreads();
   const long long F = (long long)Hkv * total;
-  if (F <= 0) return;
   const long long q = F / W;
   const unsigned r = (unsigned)(F % W);
   for (int w = t; w < W; w += 1024) {
     const long long aw = q * w + (long long)(r * (unsigned)w / (unsigned)W);  // floor(F w / W)
-    const int ap = (int)(aw / Hkv);
+    const int ap = (int)(aw / max(Hkv, 1));
     int lo = 0, hi = 1023;  // last thread whose first offset is <= ap (it holds unit aw)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
@@ -134,9 +190,12 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
       cc += su;
     }
     const int off = (int)(aw - (long long)Hkv * cc);
-    start[3 * w] = b;
-    start[3 * w + 1] = su > 0 ? off / su : 0;
-    start[3 * w + 2] = su > 0 ? off % su : 0;
+    int4 st;
+    st.x = b;
+    st.y = su > 0 ? off / su : 0;
+    st.z = su > 0 ? off % su : 0;
+    st.w = su;
+    ((int4*)(plan + 4))[w] = st;
   }
 }
 
@@ -146,7 +205,7 @@ template <int KIND, int D, int BS, int F>
 __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
-    const int32_t* __restrict__ context_lens, const int32_t* __restrict__ plan,
+    const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
     long long NB, int cap, float qk_scale, float v_scale) {
   using Ops = KvOps<KIND, D, BS>;
@@ -159,12 +218,27 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
   const int w = blockIdx.x * kWaves + uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
 
-  const int32_t* cum = plan;
-  const int32_t* start = plan + B + 1;
-  const long long Ftot = (long long)Hkv * cum[B];
+  long long Ftot;
+  int b, g, u;  // u: unit within the run
+  if (inline_plan) {
+    const Start st = wave_plan(context_lens, B, Hkv, BS, cap, W, w, lane);
+    Ftot = st.F;
+    b = st.b;
+    g = st.g;
+    u = st.u;
+    if (lane == 0) {
+      ((int4*)(plan + 4))[w] = make_int4(st.b, st.g, st.u, st.su);
+      if (w == 0) plan[0] = (int)(Ftot / Hkv);
+    }
+  } else {
+    Ftot = (long long)Hkv * plan[0];
+    const int4 st = ((const int4*)(plan + 4))[w];
+    b = uniform(st.x);
+    g = uniform(st.y);
+    u = uniform(st.z);
+  }
   const long long a = range_begin(Ftot, w, W), e = range_begin(Ftot, w + 1, W);
   if (a >= e) return;
-  int b = start[3 * w], g = start[3 * w + 1], u = start[3 * w + 2];  // u: unit within the run
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[NC];
@@ -345,108 +419,113 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
   }
 }
 
-// Merge the partials of every (b, g) run that crosses a wavefront boundary:
-// out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, M = max_w m_w.
-// The wavefronts holding the run are w0..w1; wavefront w keeps it in slot 1 if the run began
-// after the start of w's range (then it is w's last run), else in slot 0.
-template <int KIND>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(
+// Merge the partials of the runs cut by wavefront range boundaries:
+// out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, M = max_w m_w (the final normalised
+// reduction of codebumble.net, "CUDA Shared Memory Optimization").  One wavefront per boundary k
+// (between the ranges of wavefronts k and k + 1) looks at the run holding unit a_{k+1}: if that
+// run has frames on both sides and k is the first boundary that cuts its frames, the wavefront
+// merges the partials of wavefronts w0..w1 (those holding the run's first and last frames; any
+// with an empty range hold none) in wavefront order.  Wavefront w keeps a run in partial slot 1
+// if the run began after the start of w's range (it is then w's last run), else in slot 0.
+// Lane (row rr = lane / 4, quarter qd = lane % 4) merges D/4 outputs of query row rr; the loads
+// of kBatch partials are in flight together.
+template <int KIND, int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ plan, int B, int Hq, int Hkv, int G, int D, int W,
-    float v_scale) {
-  // One workgroup per (b, g); runs finished inside one stream wavefront exit at once.
-  constexpr int kPer = 8;   // outputs per thread: G * D <= 16 * 128 = 8 * 256
-  constexpr int kBatch = 4; // partials whose loads are issued together
-  const int g = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int32_t* cum = plan;
-  const int c0 = cum[b], c1 = cum[b + 1], cB = cum[B];
-  const long long F = (long long)Hkv * cB;
-  const int su = c1 - c0;  // units of each kv head's run of sequence b
-  const int nblk = su - kRestart;
-  if (su <= 0 || nblk <= 0 || F <= 0) return;
-  const long long s0 = (long long)Hkv * c0 + (long long)g * su;  // first unit of the run
-  const long long x0 = s0 + kRestart, x1 = s0 + su - 1;           // its first and last frame
+    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
+  constexpr int kBatch = 4;
+  const int k = blockIdx.x, lane = threadIdx.x;
+  const int U = plan[0];
+  const int4 st = ((const int4*)(plan + 4))[k + 1];
+  const long long F = (long long)Hkv * U;
+  const long long a1 = F * (k + 1) / W;
+  const int u = st.z, su = st.w;
+  if (a1 >= F || u <= kRestart) return;  // no frames of this run before the boundary
+  const long long s0 = a1 - u;            // first unit of the run
+  const long long x0 = s0 + kRestart, x1 = s0 + su - 1;
   // wavefront holding unit x: the largest w with floor(F w / W) <= x
   const int w0 = (int)(((x0 + 1) * W + F - 1) / F - 1);
+  if (w0 != k) return;  // an earlier boundary cuts this run
   const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
-  if (w0 == w1) return;  // finished inside one wavefront
-  const long long q = F / W;
-  const unsigned r = (unsigned)(F % W);
-  const int nout = G * D;
-  float M[kPer], num[kPer], den[kPer];
+  const int b = st.x, g = st.y;
+  // Gp = max(G, 4) rows of the group share the wavefront: lane -> (row rr, slice qd of
+  // D / lpr outputs), nv = D / (4 lpr) f32x4 per lane
+  const int Gp = G < 4 ? 4 : G;
+  const int lpr = 64 / Gp;
+  const int rr = lane / lpr, qd = lane % lpr;
+  const int nv = D / (4 * lpr);
+  constexpr int NV = D / 16;  // nv at most
+  float M = -INFINITY, den = 0.f;
+  f32x4 num[NV];
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    M[k] = -INFINITY;
-    num[k] = 0.f;
-    den[k] = 0.f;
-  }
-  // partials in wavefront order (a fixed merge order: the result does not depend on timing),
-  // kBatch at a time with all their loads in flight together
+  for (int v = 0; v < NV; ++v) num[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // Wavefront w0 keeps the run in slot 1 if the run began after the start of its range; every
+  // later wavefront's range starts inside the run (slot 0).  When F >= W no range is empty and
+  // wavefronts w0..w1 all hold a partial; otherwise empty ones are skipped.
+  const long long aw0 = F * w0 / W;
+  const bool dense = F >= W;
   for (int wb = w0; wb <= w1; wb += kBatch) {
-    int row0[kBatch];
+    f32x4 ob[kBatch][NV];
+    float mb[kBatch], lb[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int w = wb + i;
-      row0[i] = -1;
-      if (w <= w1) {
-        const long long aw = q * w + (long long)(r * (unsigned)w / (unsigned)W);
-        const long long aw1 = q * (w + 1) + (long long)(r * (unsigned)(w + 1) / (unsigned)W);
-        if (aw < aw1) row0[i] = (w * 2 + (s0 > aw ? 1 : 0)) * 16;
-      }
+      bool has = w <= w1;
+      if (!dense && has) has = F * w / W < F * (w + 1) / W;
+      const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
+      // rows past the group were never written: those lanes read nothing
+      const bool rd = has && rr < G;
+      const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
+      const f32x4* src = (const f32x4*)(ws_o + prow * D) + qd * nv;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) ob[i][v] = (rd && v < nv) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      mb[i] = rd ? ws_ml[2 * prow] : -INFINITY;
+      lb[i] = rd ? ws_ml[2 * prow + 1] : 0.f;
     }
-    float mw[kBatch][kPer], lw[kBatch][kPer], ow[kBatch][kPer];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
+    for (int i = 0; i < kBatch; ++i) {
+      if (mb[i] == -INFINITY) continue;
+      if (mb[i] > M) {
+        const float sc = __builtin_amdgcn_exp2f(M - mb[i]);
+        den *= sc;
 #pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int idx = t + 256 * k;
-        const int rr = idx / D;
-        const bool ok = row0[i] >= 0 && idx < nout;
-        const size_t prow = (size_t)(ok ? row0[i] + rr : 0);
-        mw[i][k] = ok ? ws_ml[2 * prow] : -INFINITY;
-        lw[i][k] = ok ? ws_ml[2 * prow + 1] : 0.f;
-        ow[i][k] = ok ? ws_o[prow * D + (idx - rr * D)] : 0.f;
+        for (int v = 0; v < NV; ++v) num[v] *= sc;
+        M = mb[i];
       }
+      const float ew = __builtin_amdgcn_exp2f(mb[i] - M);
+      den += ew * lb[i];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i)
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        if (mw[i][k] == -INFINITY) continue;
-        if (mw[i][k] > M[k]) {
-          const float sc = __builtin_amdgcn_exp2f(M[k] - mw[i][k]);
-          num[k] *= sc;
-          den[k] *= sc;
-          M[k] = mw[i][k];
-        }
-        const float e = __builtin_amdgcn_exp2f(mw[i][k] - M[k]);
-        num[k] += e * ow[i][k];
-        den[k] += e * lw[i][k];
-      }
+      for (int v = 0; v < NV; ++v) num[v] += ew * ob[i][v];
+    }
   }
+  if (rr >= G) return;
+  const float inv = v_scale / den;
+  const size_t o = ((size_t)b * Hq + (size_t)g * G + rr) * D + (size_t)qd * nv * 4;
 #pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int idx = t + 256 * k;
-    if (idx >= nout) break;
-    const int rr = idx / D, d = idx - rr * D;
-    const float o = num[k] / den[k] * v_scale;
-    const size_t oi = ((size_t)b * Hq + (size_t)g * G + rr) * D + d;
+  for (int v = 0; v < NV; ++v) {
+    if (v >= nv) break;
     if constexpr (KIND == KF32) {
-      ((float*)out)[oi] = o;
+      *(f32x4*)((float*)out + o + 4 * v) = num[v] * inv;
     } else {
-      ((__bf16*)out)[oi] = (__bf16)o;
+      u32x2 pk;
+      pk[0] = pack_bf16x2(num[v][0] * inv, num[v][1] * inv);
+      pk[1] = pack_bf16x2(num[v][2] * inv, num[v][3] * inv);
+      *(u32x2*)((__bf16*)out + o + 4 * v) = pk;
     }
   }
 }
 
+// Workspace: the plan (4 ints, then an int4 per wavefront), then the two partial slots of every
+// wavefront (max and sum per row, then the 16 x D accumulator rows).
 struct Layout {
   int W;
   size_t plan_bytes, ml_bytes, o_bytes;
 };
 
-Layout layout(int B, int D) {
+Layout layout(int D) {
   Layout l;
   l.W = device_compute_units() * kWgPerCu * kWaves;
-  l.plan_bytes = (((size_t)(B + 1) + 3 * (size_t)l.W) * sizeof(int32_t) + 255) / 256 * 256;
+  l.plan_bytes = ((4 + 4 * (size_t)l.W) * sizeof(int32_t) + 255) / 256 * 256;
   l.ml_bytes = (((size_t)l.W * 2 * 16 * 2) * sizeof(float) + 255) / 256 * 256;
   l.o_bytes = (size_t)l.W * 2 * 16 * D * sizeof(float);
   return l;
@@ -455,7 +534,7 @@ Layout layout(int B, int D) {
 template <int KIND, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   constexpr int F = step_frames<KIND, D, BS>();
-  const Layout l = layout(p.B, D);
+  const Layout l = layout(D);
   int32_t* plan = (int32_t*)p.workspace;
   float* ws_ml = (float*)((char*)p.workspace + l.plan_bytes);
   float* ws_o = (float*)((char*)p.workspace + l.plan_bytes + l.ml_bytes);
@@ -464,18 +543,22 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
                                                                  : p.max_blocks_per_seq * BS;
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
-  hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p.context_lens, plan, p.B,
-                     p.Hkv, BS, cap, l.W);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const bool inline_plan = p.B <= kInlinePlanMax;
+  hipError_t e;
+  if (!inline_plan) {
+    hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p.context_lens, plan,
+                       p.B, p.Hkv, BS, cap, l.W);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((decode_stream_kernel<KIND, D, BS, F>), dim3(l.W / kWaves), dim3(kWaves * 64),
                      0, stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
-                     p.block_tables, p.context_lens, plan, ws_ml, ws_o, p.B, p.max_blocks_per_seq,
-                     p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale);
+                     p.block_tables, p.context_lens, plan, inline_plan, ws_ml, ws_o, p.B,
+                     p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<KIND>), dim3(p.Hkv, p.B), dim3(256), 0, stream, p.out,
-                     ws_ml, ws_o, plan, p.B, p.Hq, p.Hkv, G, D, l.W, v_scale);
+  hipLaunchKernelGGL((decode_reduce_kernel<KIND, D>), dim3(l.W - 1), dim3(64), 0, stream, p.out,
+                     ws_ml, ws_o, plan, p.Hq, p.Hkv, G, l.W, v_scale);
   return hipGetLastError();
 }
 
@@ -492,9 +575,9 @@ hipError_t launch_kind(const DecodeParams& p, hipStream_t s) {
 
 }  // namespace
 
-size_t decode_workspace_bytes(int B, int /*Hq*/, int D, int /*bs*/, int /*kv_dtype*/,
+size_t decode_workspace_bytes(int /*B*/, int /*Hq*/, int D, int /*bs*/, int /*kv_dtype*/,
                               int /*max_context_len*/) {
-  const Layout l = layout(B, D);
+  const Layout l = layout(D);
   return l.plan_bytes + l.ml_bytes + l.o_bytes;
 }
 

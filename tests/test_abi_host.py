@@ -125,11 +125,13 @@ def test_decode_checks_the_workspace_size():
     assert decode(ws=FAKE, wsb=need - 1) == ENOSPC
 
 
-def test_decode_workspace_grows_with_the_batch_and_is_zero_for_bad_arguments():
+def test_decode_workspace_depends_on_the_launch_not_the_batch():
+    # partial slots per persistent wavefront: the size follows head_dim, not the batch
     f = lib().pa_decode_workspace_bytes
     assert f(0, 8, 128, 16, BF16, 128) == 0
     assert f(4, 8, 128, 16, BF16, 0) == 0
-    assert f(65535, 64, 128, 16, BF16, 8192) > f(4, 64, 128, 16, BF16, 8192)
+    assert f(65535, 64, 128, 16, BF16, 8192) == f(4, 64, 128, 16, BF16, 8192) > 0
+    assert f(4, 64, 64, 16, BF16, 8192) < f(4, 64, 128, 16, BF16, 8192)
 
 
 # ----------------------------------------------------------------------------- pa_prefill_chunk

@@ -275,6 +275,10 @@ STREAM_CASES = [
     ("one-sequence-over-every-wavefront", 8, 1, "bf16", 16, [100000]),
     ("thousands-of-tiny-sequences", 8, 2, "bf16", 16, "tiny"),
     ("long-and-tiny-mix-fp8", 16, 2, "fp8", 32, [1, 2, 40000, 3, 17, 33]),
+    # the largest batch planned inside the stream kernel's wavefronts, and the smallest one
+    # planned by the separate plan kernel
+    ("batch-1024-wave-planned", 8, 2, "bf16", 16, "b1024"),
+    ("batch-1025-kernel-planned", 8, 2, "bf16", 16, "b1025"),
 ]
 
 
@@ -283,6 +287,9 @@ def test_decode_stream_split_extremes(name, Hq, Hkv, kv, bs, lens):
     _say(f"stream case {name}")
     if lens == "tiny":
         lens = lambda rng: rng.integers(1, 41, size=3000)
+    elif lens in ("b1024", "b1025"):
+        nb = int(lens[1:])
+        lens = lambda rng: rng.integers(1, 400, size=nb)
     c = workloads.decode_case(name, 7, Hq=Hq, Hkv=Hkv, D=128, bs=bs, lens=lens, kv_dtype=kv,
                               std=0.7071, pool="scattered")
     g, o = GpuStep(c), OracleStep(c)
