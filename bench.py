@@ -57,6 +57,27 @@ def blas_threads() -> int:
         return 1
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per pa_decode call from the committed counter summary of this workload, if the
+    decode kernel sources are unchanged since the counters were taken (else None)."""
+    import glob
+    import hashlib
+
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.txt")):
+        try:
+            doc = json.load(open(path))
+        except (OSError, ValueError):
+            continue
+        if doc.get("workload") != workload:
+            continue
+        h = hashlib.sha256()
+        for src in doc["kernel_sources"]:
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() == doc["kernel_sources_sha256"]:
+            return int(doc["traffic_bytes_per_call"]), os.path.relpath(path, ROOT)
+    return None
+
+
 def chunk_flops(case) -> int:
     """4 * D * Hq * sum_i (pos_i + 1): QK^T and P.V over the causal key ranges, 2 FLOP per MAC."""
     ch = case.chunk
@@ -244,11 +265,16 @@ def main():
     seqs_per_s = case.B / (ms * 1e-3)
     dec_avg = float(dec_ms.mean())
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9 if case.B else 0.0
+    traffic = measured_traffic(case.name) if case.B else None
+    kernels = ("decode_stream_kernel + decode_reduce_kernel" if case.B <= 1024 else
+               "decode_plan_kernel + decode_stream_kernel + decode_reduce_kernel")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "decode_plan_kernel + decode_stream_kernel + decode_reduce_kernel (one pa_decode call)",
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic[0] if traffic else None,
+                "kernel": f"{kernels} (one pa_decode call, timed with HIP events)",
                 "avg_us": round(dec_avg * 1e3, 2),
-                "algorithmic_bytes_per_launch": kv_bytes}
+                "algorithmic_bytes_per_launch": kv_bytes,
+                "traffic_source": traffic[1] if traffic else None}
     extra = {"write_us": round(float(write_ms.mean()) * 1e3, 2),
              "decode_us": round(dec_avg * 1e3, 2),
              "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),

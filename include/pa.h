@@ -37,7 +37,8 @@
  * Shapes.  Hq query heads share Hkv KV heads in groups of G = Hq / Hkv: query head h
  *   reads KV head h / G.  Supported: D (head_dim) in {64, 128}, block_size in {16, 32},
  *   G in {1, 2, 4, 8, 16}, and (q, kv, out) dtypes (f32, f32, f32), (bf16, bf16, bf16),
- *   (bf16, fp8, bf16).  Accumulation is fp32; outputs are rounded to nearest even.
+ *   (bf16, fp8, bf16); an f32 cache with D = 128 and block_size = 32 is not supported.
+ *   Accumulation is fp32; outputs are rounded to nearest even.
  *
  * KV cache layout
  * ---------------
@@ -114,8 +115,10 @@ int pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int64_t N
                    int Hkv, int D, int block_size, pa_dtype kv_dtype, void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for this batch shape (0 is a valid answer:
- * then workspace may be NULL).  max_context_len bounds every context_lens entry.
+ * Bytes of device workspace pa_decode needs (0 only for invalid arguments).  The size follows
+ * head_dim and the device's compute-unit count, not the batch: it holds the plan of the launch
+ * and two partial-result slots per persistent wavefront.  max_context_len bounds every
+ * context_lens entry.
  */
 size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype kv_dtype,
                                  int max_context_len);
@@ -131,12 +134,14 @@ size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype 
  *   context_lens  int32 [B], each in [1, max_context_len]; the count includes the token
  *                 written this step (write it with pa_reshape_and_cache first, on the
  *                 same stream).
- *   max_context_len  host-side bound on the lengths; sizes the launch grid.
- *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, used
- *                 for the partial results of long contexts (split across the context and
- *                 merged by a second reduce kernel).  Not read before it is written.
- * Long contexts are split into partitions processed in parallel; the merge is exact up
- * to fp32 rounding.  Concurrent calls must not share a workspace.
+ *   max_context_len  host-side bound on the lengths.
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes.  Nothing
+ *                 in it is read before this call writes it; concurrent calls must not share one.
+ * The batch's (sequence, kv head, frame) work is split into equal contiguous ranges over a
+ * fixed set of persistent wavefronts; a sequence cut by a range boundary is merged from
+ * partial results by a second (reduce) kernel, exactly up to fp32 rounding ("CUDA Shared
+ * Memory Optimization": a final normalised reduction).  The merge order is fixed, so equal
+ * inputs give equal output bits.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
