@@ -28,9 +28,10 @@ namespace {
 
 constexpr int kPWaves = 4;
 constexpr int kTargetWGs = 512; // workgroups the context split aims for
+constexpr float kLazy = 8.f;    // log2-domain slack before the running shift moves
 
 // 16-row query tiles per wavefront (f32 operands take twice the registers).
-constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 2 : 4; }
+constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 2 : 2; }
 
 template <int KIND>
 struct PQ {
@@ -38,7 +39,7 @@ struct PQ {
 };
 
 template <int KIND, int D, int BS, int NT>
-__global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
+__global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_chunk_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
@@ -77,21 +78,31 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
   const int kend = min(kbeg + KS, pos0 + tq_end);
   if (kbeg >= kend) return;
 
-  // Query fragments and positions of this wavefront's NT tiles.
+  // Query fragments and positions of this wavefront's NT tiles.  A negative score scale is
+  // moved into the query's sign bits (exact), so the scores scale by qk_abs >= 0 and a row's
+  // maximum can be taken on the unscaled products.
+  const float qk_abs = fabsf(qk_scale);
+  const uint32_t qsign = qk_scale < 0.f ? (KIND == KF32 ? 0x80000000u : 0x80008000u) : 0u;
   uint32_t qw[NT][QW];
   int rpos[NT];
+  int rmin[NT];  // position of the tile's first row (the smallest), or -1 past the chunk
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int qrow = (w * NT + t) * 16 + n;
     const int tok = t0 + qrow / G;
     const bool ok = tok < C;
     rpos[t] = ok ? pos0 + tok : -1;
+    {
+      const int tok0 = t0 + (w * NT + t) * 16 / G;
+      rmin[t] = tok0 < C ? pos0 + tok0 : -1;
+    }
     const size_t row = (size_t)(r0 + (ok ? tok : 0)) * Hq + (size_t)g * G + qrow % G;
     const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
 #pragma unroll
     for (int i = 0; i < QW / 4; ++i) {
       u32x4 v = src[i];
       if (!ok) v = (u32x4){0u, 0u, 0u, 0u};
+      v ^= (u32x4){qsign, qsign, qsign, qsign};
       qw[t][4 * i] = v[0]; qw[t][4 * i + 1] = v[1]; qw[t][4 * i + 2] = v[2]; qw[t][4 * i + 3] = v[3];
     }
   }
@@ -164,33 +175,65 @@ __global__ __launch_bounds__(kPWaves * 64) void prefill_chunk_kernel(
         }
       }
     }
-    // mask, online softmax update per query row
-    typename Ops::PFrag pf[NT][NG];
+    // Online softmax per query row with a lazily moved shift: m[t] only moves (and the
+    // accumulators are rescaled) when a row's stage maximum exceeds it by more than kLazy in
+    // the log2 domain; otherwise the probabilities exp2(s - m) of the stage may exceed 1 (by at
+    // most 2^kLazy), which changes neither the normalised result nor the fp32 accumulation.
+    // One wavefront-uniform rescale decision per stage keeps the accumulators in place.  The
+    // causal / range mask is applied only on stages that reach past a row's position or the
+    // range end.
+    bool masked = key0 + 32 > kend;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) masked = masked || key0 + 31 > rmin[t];
+    if (masked) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int key = key0 + 16 * gi + 4 * j + ii;
+            s[t][gi][ii] = (key < kend && key <= rpos[t]) ? s[t][gi][ii] : -INFINITY;
+          }
+    }
+    float mxs[NT];
+    bool grow = false;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float mx = -INFINITY;
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          const int key = key0 + 16 * gi + 4 * j + ii;
-          const float v = (key < kend && key <= rpos[t]) ? s[t][gi][ii] * qk_scale : -INFINITY;
-          s[t][gi][ii] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[t][gi][ii]);
       mx = wave_max_over_j(mx);
-      const float mnew = fmaxf(m[t], mx);
-      const float msafe = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m[t] - msafe);
-      m[t] = mnew;
-      lsum[t] *= alpha;
+      mx = mx == -INFINITY ? -INFINITY : mx * qk_abs;  // scores scale by qk_abs >= 0
+      mxs[t] = mx;
+      grow = grow || mx > m[t] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
+      for (int t = 0; t < NT; ++t) {
+        const float mnew = fmaxf(m[t], mxs[t]);
+        const float alpha = m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[t] - mnew);
+        m[t] = mnew;
+        lsum[t] *= alpha;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
+      }
+    }
+    typename Ops::PFrag pf[NT][NG];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const float nm = m[t] == -INFINITY ? 0.f : -m[t];
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         f32x4 p;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(s[t][gi][ii] - msafe);
+        for (int ii = 0; ii < 4; ++ii) {
+          // a masked score is -inf: its probability is 0 whatever the scale
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][gi][ii], qk_abs, nm));
+          p[ii] = s[t][gi][ii] == -INFINITY ? 0.f : e;
+        }
         pf[t][gi] = Ops::pfrag(p, lsum[t]);
       }
     }
