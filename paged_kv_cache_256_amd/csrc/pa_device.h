@@ -256,16 +256,25 @@ struct KvOps<KF32, D, BS> {
 
 // ------------------------------------------------------------------------- wave helpers
 
+// Lanes n, n+16, n+32, n+48 hold the same query row: reduce across them.  The gfx950 row
+// swaps exchange 16-lane rows 1<->0 and 3<->2 (then 32-lane halves) between two registers, so
+// after each swap one of the pair holds the partner lanes' values -- all in the VALU, with no
+// LDS round trip.
 __device__ inline float wave_max_over_j(float x) {
-  // lanes n, n+16, n+32, n+48 hold the same query row: reduce across them
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float wave_sum_over_j(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ inline int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

@@ -26,12 +26,12 @@ namespace pa {
 
 namespace {
 
-constexpr int kPWaves = 4;
-constexpr int kTargetWGs = 512; // workgroups the context split aims for
+constexpr int kPWaves = 8;      // wavefronts per workgroup (one workgroup per compute unit)
+constexpr int kTargetWGs = 256; // workgroups the context split aims for
 constexpr float kLazy = 8.f;    // log2-domain slack before the running shift moves
 
 // 16-row query tiles per wavefront (f32 operands take twice the registers).
-constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 2 : 2; }
+constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 1 : 2; }
 
 template <int KIND>
 struct PQ {
@@ -39,7 +39,7 @@ struct PQ {
 };
 
 template <int KIND, int D, int BS, int NT>
-__global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_chunk_kernel(
+__global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
@@ -52,9 +52,10 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
   constexpr int SF = 32 / BS;            // frames per 32-key stage
   constexpr int NG = SF * KG;            // 16-key groups per stage (= 2)
   constexpr int STAGE = SF * 2 * TILE;   // bytes: [frame][K,V][tile]
-  constexpr int PPT = STAGE / 16 / (kPWaves * 64);
+  constexpr int NPIECE = STAGE / 16;                                 // 16-byte pieces per stage
+  constexpr int PPT = (NPIECE + kPWaves * 64 - 1) / (kPWaves * 64);  // pieces per thread
   static_assert(NG == 2, "a stage is two 16-key groups");
-  static_assert(PPT >= 1 && STAGE % (16 * kPWaves * 64) == 0, "stage must split over threads");
+  static_assert(NPIECE % (kPWaves * 64) == 0 || PPT == 1, "stage must split over threads");
   constexpr int QB = PQ<KIND>::bytes;
 
   __shared__ __attribute__((aligned(16))) char smem[2][STAGE];
@@ -81,7 +82,9 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
   // Query fragments and positions of this wavefront's NT tiles.  A negative score scale is
   // moved into the query's sign bits (exact), so the scores scale by qk_abs >= 0 and a row's
   // maximum can be taken on the unscaled products.
-  const float qk_abs = fabsf(qk_scale);
+  // (a zero scale is replaced by 1e-30: every product is then far below half an ulp of the
+  // row shift, so each probability is still exactly 1, and -inf * qk_abs stays -inf)
+  const float qk_abs = fmaxf(fabsf(qk_scale), 1e-30f);
   const uint32_t qsign = qk_scale < 0.f ? (KIND == KF32 ? 0x80000000u : 0x80008000u) : 0u;
   uint32_t qw[NT][QW];
   int rpos[NT];
@@ -120,7 +123,10 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
   const int nst = (kend - kbeg + 31) / 32;
   const size_t trow = (size_t)c * mbps;
 
-  // Fetch this thread's pieces of stage st (frames past kend or with invalid ids read zeros).
+  // Fetch this thread's pieces of stage st into registers.  The loads are unconditional: a
+  // frame past kend, an invalid frame id or a stage past the last reads the same 16 bytes of
+  // frame 0 in every lane (its values are masked out or never used), so no branch separates
+  // a stage's loads from the wait that consumes them.
   auto issue = [&](u32x4 (&buf)[PPT], int st) {
     const int key0 = kbeg + 32 * st;
     int fid[SF];
@@ -128,9 +134,10 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
     for (int fl = 0; fl < SF; ++fl) {
       const int fi = key0 / BS + fl;
       int f = -1;
-      if (fi * BS < kend) f = block_tables[trow + fi];
+      if (st < nst && fi * BS < kend) f = block_tables[trow + fi];
       fid[fl] = uniform((f >= 0 && (long long)f < NB) ? f : -1);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int p = threadIdx.x + k * kPWaves * 64;
@@ -141,18 +148,20 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
 #pragma unroll
       for (int z = 1; z < SF; ++z)
         if (fl == z) f = fid[z];
-      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-      if (f >= 0) {
-        const char* base = kind ? v_cache : k_cache;
-        v = *((const u32x4*)(base + ((size_t)f * Hkv + g) * TILE) + within);
-      }
-      buf[k] = v;
+      const char* base = kind ? v_cache : k_cache;
+      const u32x4* src = (f >= 0 && p < NPIECE)
+                             ? (const u32x4*)(base + ((size_t)f * Hkv + g) * TILE) + within
+                             : (const u32x4*)k_cache;
+      buf[k] = *src;
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto stash = [&](const u32x4 (&buf)[PPT], int slot) {
 #pragma unroll
-    for (int k = 0; k < PPT; ++k)
-      *((u32x4*)smem[slot] + threadIdx.x + k * kPWaves * 64) = buf[k];
+    for (int k = 0; k < PPT; ++k) {
+      const int p = threadIdx.x + k * kPWaves * 64;
+      if (NPIECE % (kPWaves * 64) == 0 || p < NPIECE) *((u32x4*)smem[slot] + p) = buf[k];
+    }
   };
 
   auto compute = [&](int st) {
@@ -230,9 +239,8 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
         f32x4 p;
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          // a masked score is -inf: its probability is 0 whatever the scale
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][gi][ii], qk_abs, nm));
-          p[ii] = s[t][gi][ii] == -INFINITY ? 0.f : e;
+          // a masked score is -inf and qk_abs > 0: its probability is exactly 0
+          p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][gi][ii], qk_abs, nm));
         }
         pf[t][gi] = Ops::pfrag(p, lsum[t]);
       }
@@ -262,12 +270,13 @@ __global__ __launch_bounds__(kPWaves * 64, KIND == KF32 ? 1 : 2) void prefill_ch
     }
   };
 
+  // One stage in flight in registers while the previous one is computed from LDS.
   u32x4 pre[PPT];
   issue(pre, 0);
   stash(pre, 0);
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
-    if (st + 1 < nst) issue(pre, st + 1);
+    issue(pre, st + 1);
     compute(st);
     if (st + 1 < nst) stash(pre, (st + 1) & 1);
     __syncthreads();
