@@ -46,10 +46,11 @@ __host__ __device__ constexpr uint32_t v_tile_byte(int o, int d, int D, int b) {
 
 // ------------------------------------------------------------------------- conversions
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  // fptrunc lowers to v_cvt_pk_bf16_f32 (round to nearest even) on gfx950
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  // a two-wide fptrunc is one v_cvt_pk_bf16_f32 (round to nearest even) on gfx950
+  const bf16x2 v = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

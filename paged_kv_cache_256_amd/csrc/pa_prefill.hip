@@ -51,14 +51,18 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
   constexpr int TILE = Ops::TILE;
   constexpr int SF = 32 / BS;            // frames per 32-key stage
   constexpr int NG = SF * KG;            // 16-key groups per stage (= 2)
-  constexpr int STAGE = SF * 2 * TILE;   // bytes: [frame][K,V][tile]
+  constexpr int STAGE = SF * 2 * TILE;   // bytes of K and V per stage
+  // bf16: K tiles [frame][tile] then V as the P.V operands: for head-dim block cc and lane l,
+  // 16 bytes = the 4 keys of 16-key group 0 then those of group 1 (one LDS read per MFMA).
+  // f32 / fp8: [frame][K, V][tile].
+  constexpr bool PAIRV = KIND == KBF16;
   constexpr int NPIECE = STAGE / 16;                                 // 16-byte pieces per stage
   constexpr int PPT = (NPIECE + kPWaves * 64 - 1) / (kPWaves * 64);  // pieces per thread
   static_assert(NG == 2, "a stage is two 16-key groups");
   static_assert(NPIECE % (kPWaves * 64) == 0 || PPT == 1, "stage must split over threads");
   constexpr int QB = PQ<KIND>::bytes;
 
-  __shared__ __attribute__((aligned(16))) char smem[2][STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[3][STAGE];
 
   const int x = blockIdx.x, qt = blockIdx.y;
   const int c = blockIdx.z / Hkv, g = blockIdx.z % Hkv;
@@ -160,19 +164,41 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
 #pragma unroll
     for (int k = 0; k < PPT; ++k) {
       const int p = threadIdx.x + k * kPWaves * 64;
-      if (NPIECE % (kPWaves * 64) == 0 || p < NPIECE) *((u32x4*)smem[slot] + p) = buf[k];
+      if (!(NPIECE % (kPWaves * 64) == 0 || p < NPIECE)) continue;
+      if constexpr (PAIRV) {
+        const int fl = p / (2 * TILE / 16);
+        const int kind = (p / (TILE / 16)) & 1;
+        const int within = p % (TILE / 16);
+        if (kind == 0) {
+          *((u32x4*)(smem[slot] + fl * TILE) + within) = buf[k];
+        } else {
+          // piece r of the V tile holds quads u = 2r, 2r + 1 (u = key group h * NC + block c)
+          const int r = within >> 6, ll = within & 63;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int u = 2 * r + half;
+            const int gk = fl * KG + u / NC, cc = u % NC;
+            u32x2 v;
+            v[0] = buf[k][2 * half];
+            v[1] = buf[k][2 * half + 1];
+            *(u32x2*)(smem[slot] + SF * TILE + ((cc * 64 + ll) * 2 + gk) * 8) = v;
+          }
+        }
+      } else {
+        *((u32x4*)smem[slot] + p) = buf[k];
+      }
     }
   };
 
-  auto compute = [&](int st) {
-    const char* sb = smem[st & 1];
-    const int key0 = kbeg + 32 * st;
-    f32x4 s[NT][NG];
+  // Scores of stage st (K from LDS buffer st % 3).
+  auto qk = [&](int st, f32x4 (&s)[NT][NG]) {
+    const char* sb = smem[st % 3];
 #pragma unroll
     for (int fl = 0; fl < SF; ++fl) {
       u32x4 kt[NL];
 #pragma unroll
-      for (int r = 0; r < NL; ++r) kt[r] = *((const u32x4*)(sb + (2 * fl) * TILE + r * 1024) + lane);
+      for (int r = 0; r < NL; ++r)
+        kt[r] = *((const u32x4*)(sb + (PAIRV ? fl : 2 * fl) * TILE + r * 1024) + lane);
 #pragma unroll
       for (int h = 0; h < KG; ++h) {
 #pragma unroll
@@ -183,6 +209,21 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
           s[t][fl * KG + h] = a;
         }
       }
+    }
+  };
+
+  // Softmax and P.V of stage st (V from LDS buffer st % 3).  `overlap` runs between the
+  // shift update and the exponentials, in the same basic block as the exponentials and the
+  // P.V products, so that the score MFMAs it issues for the next stage interleave with them.
+  auto finish = [&](int st, f32x4 (&s)[NT][NG], auto&& overlap) {
+    const char* sb = smem[st % 3];
+    const int key0 = kbeg + 32 * st;
+    // V operands of the stage (bf16: read before the softmax so that their latency hides
+    // behind it)
+    u32x4 vp[PAIRV ? NC : 1];
+    if constexpr (PAIRV) {
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) vp[cc] = *((const u32x4*)(sb + SF * TILE) + cc * 64 + lane);
     }
     // Online softmax per query row with a lazily moved shift: m[t] only moves (and the
     // accumulators are rescaled) when a row's stage maximum exceeds it by more than kLazy in
@@ -204,6 +245,20 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
             const int key = key0 + 16 * gi + 4 * j + ii;
             s[t][gi][ii] = (key < kend && key <= rpos[t]) ? s[t][gi][ii] : -INFINITY;
           }
+      if constexpr (PAIRV) {
+        // keys past the range end may be unwritten slots: clear their values
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
+          const uint32_t m0 = keep >= 2 ? 0xffffffffu : (keep == 1 ? 0x0000ffffu : 0u);
+          const uint32_t m1 = keep >= 4 ? 0xffffffffu : (keep == 3 ? 0x0000ffffu : 0u);
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) {
+            vp[cc][2 * gi] &= m0;
+            vp[cc][2 * gi + 1] &= m1;
+          }
+        }
+      }
     }
     float mxs[NT];
     bool grow = false;
@@ -230,6 +285,7 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
         for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
       }
     }
+    overlap();
     typename Ops::PFrag pf[NT][NG];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -246,39 +302,63 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
       }
     }
     // P * V
-    u32x4 vt[SF][NL];
+    if constexpr (PAIRV) {
 #pragma unroll
-    for (int fl = 0; fl < SF; ++fl)
+      for (int t = 0; t < NT; ++t) {
+        u32x4 pb;
+        pb[0] = pf[t][0][0]; pb[1] = pf[t][0][1]; pb[2] = pf[t][1][0]; pb[3] = pf[t][1][1];
 #pragma unroll
-      for (int r = 0; r < NL; ++r) vt[fl][r] = *((const u32x4*)(sb + (2 * fl + 1) * TILE + r * 1024) + lane);
-    if (key0 + 32 > kend) {
-      // keys past the range end may be unwritten slots: clear their values
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[gi / KG], gi % KG, cc, keep);
+        for (int cc = 0; cc < NC; ++cc) acc[t][cc] = mfma_x32_bf16(vp[cc], pb, acc[t][cc]);
       }
-    }
+    } else {
+      u32x4 vt[SF][NL];
 #pragma unroll
-    for (int cc = 0; cc < NC; ++cc) {
-      const auto va = Ops::vop(vt[0], 0, cc);
-      const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
+      for (int fl = 0; fl < SF; ++fl)
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
+        for (int r = 0; r < NL; ++r) vt[fl][r] = *((const u32x4*)(sb + (2 * fl + 1) * TILE + r * 1024) + lane);
+      if (key0 + 32 > kend) {
+        // keys past the range end may be unwritten slots: clear their values
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[gi / KG], gi % KG, cc, keep);
+        }
+      }
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) {
+        const auto va = Ops::vop(vt[0], 0, cc);
+        const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
+      }
     }
   };
 
-  // One stage in flight in registers while the previous one is computed from LDS.
+  // Software pipeline over a ring of three LDS stages: while the softmax and P.V of stage st
+  // run on the vector ALUs, the score MFMAs of stage st + 1 are already issued, and stage
+  // st + 2 moves from registers into LDS; stage st + 3 is in flight from memory.
   u32x4 pre[PPT];
   issue(pre, 0);
   stash(pre, 0);
+  issue(pre, 1);
+  stash(pre, 1);
+  issue(pre, 2);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    issue(pre, st + 1);
-    compute(st);
-    if (st + 1 < nst) stash(pre, (st + 1) & 1);
+  f32x4 sa[NT][NG], sz[NT][NG];
+  qk(0, sa);
+  for (int st = 0; st < nst; st += 2) {
+    // (past the last stage the next-stage scores read a ring buffer already written and are
+    // never used: issuing them unconditionally keeps them in the exponentials' block)
+    finish(st, sa, [&] { qk(st + 1, sz); });
+    if (st + 2 < nst) stash(pre, (st + 2) % 3);
+    issue(pre, st + 3);
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    finish(st + 1, sz, [&] { qk(st + 2, sa); });
+    if (st + 3 < nst) stash(pre, (st + 3) % 3);
+    issue(pre, st + 4);
     __syncthreads();
   }
 
