@@ -204,6 +204,56 @@ int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_se
                               int num_chunks, int block_size, int64_t NB, int max_chunk_len,
                               int max_context_len);
 
+/*
+ * Host-side block manager (no GPU involved): the bookkeeping that produces the block tables,
+ * slot mappings and copy-on-write pairs the calls above consume.  It follows
+ * codebumble.net, "The Block Table Mapping Subsystem" (a global free list; a position splits
+ * into logical block = pos / block_size and offset = pos % block_size; a frame is taken from
+ * the free list when a token starts a block), bicarait.com, "Architectural Blueprint 2" and
+ * infoisland, section 2 (branches of one prompt reference the same frames; a frame is copied
+ * only when a branch writes into it while others still reference it).
+ *   Frames: 0 .. num_frames-1, initially all free in increasing order; allocation takes the
+ *     head of the free list, a frame whose last reference is dropped goes to its tail.
+ *   Sequences are named by caller-chosen int64 ids.  A handle is not thread safe: callers
+ *     serialise calls on one handle.  Every mutating call either succeeds completely or
+ *     changes nothing (PA_ENOSPC when the free list is too short, PA_EINVAL for unknown or
+ *     duplicate ids).
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* Create a manager of num_frames frames of block_size tokens; *out receives the handle. */
+int pa_bm_create(int64_t num_frames, int block_size, pa_block_manager** out);
+/* Destroy a handle (NULL is allowed). */
+void pa_bm_destroy(pa_block_manager* bm);
+
+/*
+ * Append one token to each listed sequence, in list order (an id listed k times gets k
+ * tokens; an unknown id starts a new sequence).  slots[i] (int64 [n]) receives the cache slot
+ * frame * block_size + offset of entry i's token.  When a token goes into a frame other
+ * sequences still reference, the writer first moves to a fresh frame: the pair (old, new) is
+ * appended to copy_pairs (int64 [n][2], room for n pairs) and *num_copies counts them.  Apply
+ * the copies (pa_copy_blocks) before writing the tokens (pa_reshape_and_cache).
+ */
+int pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int64_t n, int64_t* slots,
+                 int64_t* copy_pairs, int64_t* num_copies);
+/* The child (a new id) references every frame of the parent and has its length. */
+int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+/* Drop a sequence; frames no other sequence references return to the free list. */
+int pa_bm_free(pa_block_manager* bm, int64_t seq);
+/* Queries: free frames, a sequence's token count, a frame's reference count, and the free
+ * list in allocation order (capacity entries of room; *count receives the length). */
+int pa_bm_num_free(const pa_block_manager* bm, int64_t* out);
+int pa_bm_seq_len(const pa_block_manager* bm, int64_t seq, int64_t* out);
+int pa_bm_ref_count(const pa_block_manager* bm, int64_t frame, int32_t* out);
+int pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int64_t capacity, int64_t* count);
+/*
+ * Block tables and context lengths of n sequences for pa_decode / pa_prefill_chunk:
+ * tables (int32 [n][max_blocks_per_seq], entries past a sequence's blocks are -1) and
+ * context_lens (int32 [n], tokens written so far).  PA_ERANGE if a sequence has more blocks.
+ */
+int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int64_t n,
+                       int32_t* tables, int max_blocks_per_seq, int32_t* context_lens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,6 +21,9 @@ Sources (the pages this method is described on):
   * "High-Throughput LLM Serving with vLLM & PagedAttention" (infoisland),
     sections 2 (copy-on-write), 4 (fp8 KV cache) and 5 (512-token chunks).
 
+oracle.block_manager holds the reference model of the host block manager (free list,
+on-demand allocation, fork, copy-on-write, release), pinned in tests/test_block_manager.py.
+
 Parity status of each function is stated in its docstring; every function is
 pinned by tests in tests/test_oracle.py against values the pages print,
 closed forms, library routines on special cases or brute force.
@@ -46,3 +49,4 @@ from .paged_attention import (  # noqa: F401
     prefill_chunk,
     slot_of,
 )
+from .block_manager import BlockManagerModel, OutOfBlocks  # noqa: F401

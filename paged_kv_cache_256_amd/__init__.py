@@ -7,10 +7,12 @@ declared in include/pa.h:
     copy_blocks        duplicate frames for copy-on-write
     decode             paged GQA decode attention (split over the context + reduce)
     prefill_chunk      causal attention of prefill chunks over their paged context
+    BlockManager       host-side frames, block tables, slots and copy-on-write pairs
 """
 
 from ._binding import (  # noqa: F401
     EXPORTED,
+    BlockManager,
     LIB_PATH,
     PAError,
     build_info,

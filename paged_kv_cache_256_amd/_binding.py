@@ -54,6 +54,16 @@ _SIGS = {
     "pa_validate_slots": ([_P, _I64, _I64, _I], _I),
     "pa_validate_copy_pairs": ([_P, _I64, _I64], _I),
     "pa_validate_chunk_indices": ([_P, _I, _P, _P, _I, _I, _I64, _I, _I], _I),
+    "pa_bm_create": ([_I64, _I, _P], _I),
+    "pa_bm_destroy": ([_P], None),
+    "pa_bm_append": ([_P, _P, _I64, _P, _P, _P], _I),
+    "pa_bm_fork": ([_P, _I64, _I64], _I),
+    "pa_bm_free": ([_P, _I64], _I),
+    "pa_bm_num_free": ([_P, _P], _I),
+    "pa_bm_seq_len": ([_P, _I64, _P], _I),
+    "pa_bm_ref_count": ([_P, _I64, _P], _I),
+    "pa_bm_free_list": ([_P, _P, _I64, _P], _I),
+    "pa_bm_block_tables": ([_P, _P, _I64, _P, _I, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -248,3 +258,80 @@ def validate_chunk_indices(block_tables, query_start_loc, context_lens, block_si
     cl, pcl = _host(context_lens, np.int32)
     _check(_lib.pa_validate_chunk_indices(pbt, bt.shape[1], pqs, pcl, cl.shape[0], block_size, NB,
                                           int(max_chunk_len), int(max_context_len)))
+
+
+# ----------------------------------------------------------------------------- block manager
+
+
+class BlockManager:
+    """Handle of the library's host-side block manager (pa_bm_* in pa.h): frames, block tables,
+    slots and copy-on-write pairs for the GPU calls.  Arguments and results are numpy arrays."""
+
+    def __init__(self, num_frames: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(_lib.pa_bm_create(int(num_frames), int(block_size), ctypes.byref(h)))
+        self._h = h
+        self.num_frames = int(num_frames)
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            _lib.pa_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def append(self, seq_ids):
+        """One token per listed id (in order); returns (slots int64 [n], copy_pairs int64 [k, 2])."""
+        ids, pids = _host(seq_ids, np.int64)
+        ids = ids.reshape(-1)
+        n = ids.shape[0]
+        slots = np.empty(n, np.int64)
+        pairs = np.empty((max(n, 1), 2), np.int64)
+        nc = ctypes.c_int64(0)
+        _check(_lib.pa_bm_append(self._h, pids, n, ctypes.c_void_p(slots.ctypes.data),
+                                 ctypes.c_void_p(pairs.ctypes.data), ctypes.byref(nc)))
+        return slots, pairs[:nc.value].copy()
+
+    def fork(self, parent: int, child: int):
+        _check(_lib.pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq: int):
+        _check(_lib.pa_bm_free(self._h, int(seq)))
+
+    def num_free(self) -> int:
+        v = ctypes.c_int64(0)
+        _check(_lib.pa_bm_num_free(self._h, ctypes.byref(v)))
+        return v.value
+
+    def seq_len(self, seq: int) -> int:
+        v = ctypes.c_int64(0)
+        _check(_lib.pa_bm_seq_len(self._h, int(seq), ctypes.byref(v)))
+        return v.value
+
+    def ref_count(self, frame: int) -> int:
+        v = ctypes.c_int32(0)
+        _check(_lib.pa_bm_ref_count(self._h, int(frame), ctypes.byref(v)))
+        return v.value
+
+    def free_list(self) -> np.ndarray:
+        out = np.empty(self.num_frames, np.int32)
+        cnt = ctypes.c_int64(0)
+        _check(_lib.pa_bm_free_list(self._h, ctypes.c_void_p(out.ctypes.data), self.num_frames,
+                                    ctypes.byref(cnt)))
+        return out[:cnt.value].copy()
+
+    def block_tables(self, seq_ids, max_blocks_per_seq: int):
+        """(tables int32 [n, max_blocks_per_seq] padded with -1, context_lens int32 [n])."""
+        ids, pids = _host(seq_ids, np.int64)
+        ids = ids.reshape(-1)
+        n = ids.shape[0]
+        tables = np.empty((n, int(max_blocks_per_seq)), np.int32)
+        lens = np.empty(n, np.int32)
+        _check(_lib.pa_bm_block_tables(self._h, pids, n, ctypes.c_void_p(tables.ctypes.data),
+                                       int(max_blocks_per_seq), ctypes.c_void_p(lens.ctypes.data)))
+        return tables, lens

@@ -15,10 +15,10 @@
 #include "pa_internal.h"
 
 namespace {
-
 thread_local std::string g_error;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int pa::set_error(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -28,10 +28,19 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-int ok() {
+int pa::clear_error() {
   g_error.clear();
   return PA_OK;
 }
+
+namespace {
+
+template <typename... A>
+int fail(int code, const char* fmt, A... a) {
+  return pa::set_error(code, fmt, a...);
+}
+
+int ok() { return pa::clear_error(); }
 
 int hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();

@@ -47,6 +47,11 @@ struct PrefillParams {
   void* workspace;
 };
 
+// The calling thread's error message (pa_last_error): set_error formats it and returns `code`,
+// clear_error empties it and returns PA_OK.
+int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int clear_error();
+
 // Compute units of the current device (cached per device; 256 when no device is visible).
 int device_compute_units();
 

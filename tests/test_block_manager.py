@@ -1,0 +1,328 @@
+"""Host block manager: the reference model pinned to what the pages fix, then the library's
+C++ manager (through the C ABI) against the model, bit for bit, on seeded operation streams.
+
+Pins of the model (each would fail for a plausible mistake in it):
+  * the page's allocation example: 48 tokens of a first sequence land in frames 0, 1, 2 taken
+    from the head of the free list (codebumble.net, "The Block Table Mapping Subsystem");
+  * content: replaying every call -- copies first, then token writes -- each live sequence
+    reads back exactly its own token history through its block table (what copy-on-write must
+    preserve: infoisland, section 2);
+  * sharing: branches of one prompt use the prompt's frames once (bicarait.com, "Architectural
+    Blueprint 2"); N + 1 sequences sharing a partly filled last frame that all append one token
+    make exactly N copies;
+  * waste stays inside the last frame of each sequence (infoisland, section 2);
+  * every frame is either free or used, never both, and released frames return to the list.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_256_amd as pa
+from oracle import BlockManagerModel, OutOfBlocks
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+class Replay:
+    """Token contents of the cache, by slot, rebuilt from the manager's outputs."""
+
+    def __init__(self, bs):
+        self.bs = bs
+        self.cache = {}
+        self.history = {}
+
+    def apply(self, seq_ids, slots, copies):
+        for src, dst in copies:
+            for o in range(self.bs):
+                if src * self.bs + o in self.cache:
+                    self.cache[dst * self.bs + o] = self.cache[src * self.bs + o]
+                else:
+                    self.cache.pop(dst * self.bs + o, None)
+        for s, slot in zip(seq_ids, slots):
+            h = self.history.setdefault(int(s), [])
+            token = (int(s), len(h))
+            h.append(token)
+            self.cache[int(slot)] = token
+
+    def fork(self, parent, child):
+        self.history[child] = list(self.history[parent])
+
+    def release(self, seq):
+        del self.history[seq]
+
+    def check(self, table_of):
+        for s, h in self.history.items():
+            table = table_of(s)
+            for pos, token in enumerate(h):
+                assert self.cache.get(table[pos // self.bs] * self.bs + pos % self.bs) == token, (s, pos)
+
+
+def test_model_page_example_first_frames():
+    ex = json.load(open(os.path.join(HERE, "golden", "page_examples.json")))["allocate_slot"]
+    m = BlockManagerModel(ex["num_physical_blocks"], ex["block_size"])
+    slots, copies = m.append([7] * 48)
+    assert copies == []
+    assert m.tables[7] == ex["first_sequence_frames"]
+    bs = ex["block_size"]
+    assert slots == [ex["first_sequence_frames"][p // bs] * bs + p % bs for p in range(48)]
+
+
+def _next_op(rng, live, next_id, max_seqs=12):
+    """A seeded random operation on the current live sequences: (op, args, next_id)."""
+    r = rng.random()
+    if not live or r < 0.15:
+        return "append", [next_id] * int(rng.integers(1, 40)), next_id + 1
+    if r < 0.30 and len(live) < max_seqs:
+        return "fork", (int(rng.choice(live)), next_id), next_id + 1
+    if r < 0.42 and len(live) > 1:
+        return "release", int(rng.choice(live)), next_id
+    k = int(rng.integers(1, len(live) + 1))
+    return "append", [int(x) for x in rng.choice(live, size=k)], next_id
+
+
+@pytest.mark.parametrize("seed,bs", [(1, 4), (2, 16), (3, 1), (4, 32)])
+def test_model_content_waste_and_conservation(seed, bs):
+    rng = np.random.default_rng(seed)
+    nb = 400
+    m = BlockManagerModel(nb, bs)
+    rep = Replay(bs)
+    next_id = 0
+    for _ in range(150):
+        op, arg, next_id = _next_op(rng, sorted(m.tables), next_id)
+        if op == "append":
+            try:
+                slots, copies = m.append(arg)
+            except OutOfBlocks:
+                continue
+            rep.apply(arg, slots, copies)
+        elif op == "fork":
+            m.fork(*arg)
+            rep.fork(*arg)
+        else:
+            m.release(arg)
+            rep.release(arg)
+        rep.check(lambda s: m.tables[s])
+        used = {b for t in m.tables.values() for b in t}
+        assert len(set(m.free)) == len(m.free) and not (used & set(m.free))
+        assert len(used) + len(m.free) == nb
+        for s, t in m.tables.items():
+            assert len(set(t)) == len(t)
+            assert 0 <= len(t) * bs - m.lengths[s] < bs
+
+
+@pytest.mark.parametrize("prompt,branches,bs", [(64, 4, 16), (70, 4, 16), (5, 3, 4)])
+def test_model_sharing_and_copy_count(prompt, branches, bs):
+    m = BlockManagerModel(200, bs)
+    m.append([0] * prompt)
+    for b in range(1, branches + 1):
+        m.fork(0, b)
+    prompt_frames = -(-prompt // bs)
+    assert len({f for t in m.tables.values() for f in t}) == prompt_frames
+    _, copies = m.append(list(range(branches + 1)))
+    assert len(copies) == (0 if prompt % bs == 0 else branches)
+    # the shared prompt frames are still stored once
+    full = prompt // bs
+    assert all(t[:full] == m.tables[0][:full] for t in m.tables.values())
+
+
+def test_model_release_returns_frames_to_the_tail():
+    m = BlockManagerModel(6, 2)
+    m.append([0] * 4)            # frames 0, 1
+    m.append([1] * 2)            # frame 2
+    m.release(0)
+    assert m.free == [3, 4, 5, 0, 1]
+
+
+def test_model_out_of_blocks_changes_nothing():
+    m = BlockManagerModel(3, 2)
+    m.append([0] * 5)            # frames 0, 1, 2
+    before = (list(m.free), {k: list(v) for k, v in m.tables.items()}, dict(m.lengths))
+    with pytest.raises(OutOfBlocks):
+        m.append([0, 1])         # seq 0 opens frame 3 (none left)
+    assert (m.free, m.tables, m.lengths) == before
+
+
+# ----------------------------------------------------------------------------- library vs model
+
+
+def _compare(bm, m, seqs):
+    assert list(bm.free_list()) == m.free
+    assert bm.num_free() == len(m.free)
+    if seqs:
+        width = max(1, max(len(m.tables[s]) for s in seqs))
+        tables, lens = bm.block_tables(seqs, width)
+        for i, s in enumerate(seqs):
+            want, L = m.block_table(s, width)
+            assert list(tables[i]) == want and lens[i] == L
+    for f in range(bm.num_frames):
+        assert bm.ref_count(f) == m.users(f)
+
+
+@pytest.mark.parametrize("seed,bs,nb", [(11, 4, 120), (12, 16, 300), (13, 1, 90), (14, 32, 60)])
+def test_library_matches_model(seed, bs, nb):
+    rng = np.random.default_rng(seed)
+    m = BlockManagerModel(nb, bs)
+    bm = pa.BlockManager(nb, bs)
+    live = []
+    next_id = 0
+    for _ in range(200):
+        op, arg, next_id = _next_op(rng, sorted(m.tables), next_id)
+        if op == "append":
+            try:
+                want_slots, want_copies = m.append(arg)
+            except OutOfBlocks:
+                with pytest.raises(pa.PAError, match="ENOSPC"):
+                    bm.append(arg)
+                _compare(bm, m, live)
+                continue
+            slots, copies = bm.append(arg)
+            assert list(slots) == want_slots
+            assert [tuple(c) for c in copies] == want_copies
+            live.extend(s for s in dict.fromkeys(arg) if s not in live)
+        elif op == "fork":
+            m.fork(*arg)
+            bm.fork(*arg)
+            live.append(arg[1])
+        else:
+            m.release(arg)
+            bm.free(arg)
+            live.remove(arg)
+        _compare(bm, m, live)
+        for s in live:
+            assert bm.seq_len(s) == m.lengths[s]
+    bm.close()
+
+
+def test_library_errors():
+    bm = pa.BlockManager(4, 2)
+    bm.append([0, 0, 0])
+    with pytest.raises(pa.PAError, match="unknown parent"):
+        bm.fork(9, 1)
+    bm.fork(0, 1)
+    with pytest.raises(pa.PAError, match="already exists"):
+        bm.fork(0, 1)
+    with pytest.raises(pa.PAError, match="unknown sequence"):
+        bm.free(5)
+    with pytest.raises(pa.PAError, match="ERANGE"):
+        bm.block_tables([0], 1)
+    with pytest.raises(pa.PAError, match="ERANGE"):
+        bm.ref_count(4)
+    free_before = list(bm.free_list())
+    with pytest.raises(pa.PAError, match="ENOSPC"):
+        bm.append([0, 1, 0, 1, 0, 1, 0, 1])
+    assert list(bm.free_list()) == free_before and bm.seq_len(0) == 3
+    with pytest.raises(pa.PAError, match="EINVAL"):
+        pa.BlockManager(0, 16)
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+
+class _FreeToHead(BlockManagerModel):
+    def release(self, seq):
+        table = self.tables.pop(seq)
+        del self.lengths[seq]
+        for b in reversed(table):
+            if self.users(b) == 0:
+                self.free.insert(0, b)
+
+
+class _NeverCopy(BlockManagerModel):
+    def users(self, block):
+        return 1
+
+
+class _AlwaysCopy(BlockManagerModel):
+    def users(self, block):
+        return 2
+
+
+class _AllocateFromTail(BlockManagerModel):
+    def _write_one(self, seq):
+        self.free.reverse()
+        try:
+            return super()._write_one(seq)
+        finally:
+            self.free.reverse()
+
+
+class _SlotOffByOne(BlockManagerModel):
+    def _write_one(self, seq):
+        slot, copy = super()._write_one(seq)
+        return slot + 1, copy
+
+
+def _pins(cls):
+    """Run every model pin against `cls`; returns the names of the pins that fail."""
+    failed = []
+    pins = {
+        "page example": lambda: _pin_page_example(cls),
+        "content": lambda: _pin_content(cls),
+        "copy count": lambda: _pin_copy_count(cls),
+        "release order": lambda: _pin_release_order(cls),
+    }
+    for name, f in pins.items():
+        try:
+            f()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def _pin_page_example(cls):
+    ex = json.load(open(os.path.join(HERE, "golden", "page_examples.json")))["allocate_slot"]
+    m = cls(ex["num_physical_blocks"], ex["block_size"])
+    slots, _ = m.append([7] * 48)
+    bs = ex["block_size"]
+    assert m.tables[7] == ex["first_sequence_frames"]
+    assert slots == [ex["first_sequence_frames"][p // bs] * bs + p % bs for p in range(48)]
+
+
+def _pin_content(cls):
+    rng = np.random.default_rng(5)
+    m, rep, next_id = cls(300, 4), Replay(4), 0
+    for _ in range(120):
+        op, arg, next_id = _next_op(rng, sorted(m.tables), next_id)
+        if op == "append":
+            try:
+                slots, copies = m.append(arg)
+            except OutOfBlocks:
+                continue
+            rep.apply(arg, slots, copies)
+        elif op == "fork":
+            m.fork(*arg)
+            rep.fork(*arg)
+        else:
+            m.release(arg)
+            rep.release(arg)
+        rep.check(lambda s: m.tables[s])
+
+
+def _pin_copy_count(cls):
+    m = cls(200, 16)
+    m.append([0] * 70)
+    for b in range(1, 5):
+        m.fork(0, b)
+    _, copies = m.append(list(range(5)))
+    assert len(copies) == 4
+
+
+def _pin_release_order(cls):
+    m = cls(6, 2)
+    m.append([0] * 4)
+    m.append([1] * 2)
+    m.release(0)
+    assert m.free == [3, 4, 5, 0, 1]
+
+
+def test_pins_pass_on_the_model():
+    assert _pins(BlockManagerModel) == []
+
+
+@pytest.mark.parametrize("mutant", [_FreeToHead, _NeverCopy, _AlwaysCopy, _AllocateFromTail,
+                                    _SlotOffByOne], ids=lambda c: c.__name__)
+def test_planted_mistake_is_caught(mutant):
+    assert _pins(mutant), f"no pin catches {mutant.__name__}"
