@@ -236,6 +236,19 @@ void pa_bm_destroy(pa_block_manager* bm);
  */
 int pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int64_t n, int64_t* slots,
                  int64_t* copy_pairs, int64_t* num_copies);
+/*
+ * Prefix caching (codebumble.net, "CUDA Shared Memory Optimization": a prefix tree of token
+ * blocks lets a prompt reuse the blocks an earlier prompt computed).  Start sequence `seq` (a new
+ * id) with the n prompt tokens `tokens` (int32 ids).  The prompt's leading full blocks that match
+ * a registered block chain -- same token ids, block by block, from the first block on -- are
+ * referenced instead of allocated; *num_cached receives their token count (a multiple of
+ * block_size: their K/V are already in the cache and need no prefill).  The other blocks are
+ * allocated; the full ones are registered for later prompts.  slots (int64 [n]) receives every
+ * token's slot.  A registered frame that is released stays matchable while it waits in the
+ * free list and is dropped from the tree when allocation reuses it.
+ */
+int pa_bm_append_prompt(pa_block_manager* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                        int64_t* slots, int64_t* num_cached);
 /* The child (a new id) references every frame of the parent and has its length. */
 int pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
 /* Drop a sequence; frames no other sequence references return to the free list. */

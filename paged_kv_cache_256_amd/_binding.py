@@ -57,6 +57,7 @@ _SIGS = {
     "pa_bm_create": ([_I64, _I, _P], _I),
     "pa_bm_destroy": ([_P], None),
     "pa_bm_append": ([_P, _P, _I64, _P, _P, _P], _I),
+    "pa_bm_append_prompt": ([_P, _I64, _P, _I64, _P, _P], _I),
     "pa_bm_fork": ([_P, _I64, _I64], _I),
     "pa_bm_free": ([_P, _I64], _I),
     "pa_bm_num_free": ([_P, _P], _I),
@@ -296,6 +297,16 @@ class BlockManager:
         _check(_lib.pa_bm_append(self._h, pids, n, ctypes.c_void_p(slots.ctypes.data),
                                  ctypes.c_void_p(pairs.ctypes.data), ctypes.byref(nc)))
         return slots, pairs[:nc.value].copy()
+
+    def append_prompt(self, seq: int, tokens):
+        """Start `seq` with prompt token ids; returns (slots int64 [n], cached token count)."""
+        t, pt = _host(tokens, np.int32)
+        n = t.reshape(-1).shape[0]
+        slots = np.empty(n, np.int64)
+        cached = ctypes.c_int64(0)
+        _check(_lib.pa_bm_append_prompt(self._h, int(seq), pt, n, ctypes.c_void_p(slots.ctypes.data),
+                                        ctypes.byref(cached)))
+        return slots, cached.value
 
     def fork(self, parent: int, child: int):
         _check(_lib.pa_bm_fork(self._h, int(parent), int(child)))

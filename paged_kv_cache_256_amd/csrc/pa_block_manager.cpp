@@ -14,28 +14,99 @@
 //    returned so the caller copies the frame's contents with pa_copy_blocks before writing.
 //  * free(s) drops one reference from each of s's frames; frames no table references any more
 //    return to the free list in table order.
+//  * Prefix caching (codebumble.net, "CUDA Shared Memory Optimization": a prefix tree of token
+//    blocks lets a new prompt reference the blocks an earlier prompt already computed):
+//    append_prompt matches the prompt's full blocks in a tree whose nodes are keyed by
+//    (parent node, the block's token ids) -- compared exactly, so no two different prefixes can
+//    share a frame -- references every matched frame, and registers the full blocks it fills.
+//    A released frame keeps its registration while it waits in the free list (a later prompt
+//    can revive it) and loses it when allocation reuses the frame.
 // Every mutating call either succeeds completely or changes nothing.
 
 #include <climits>
 #include <cstdint>
 #include <deque>
+#include <functional>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
 
+namespace {
+
+// A prefix-tree edge: the parent node (-1 for a prompt's first block) and the block's tokens.
+struct BlockKey {
+  int64_t parent = -1;
+  std::vector<int32_t> tokens;
+  bool operator==(const BlockKey& o) const { return parent == o.parent && tokens == o.tokens; }
+};
+struct BlockKeyHash {
+  size_t operator()(const BlockKey& k) const {
+    uint64_t h = 0x9e3779b97f4a7c15ull ^ (uint64_t)k.parent;
+    for (int32_t t : k.tokens) h = (h ^ (uint32_t)t) * 0x100000001b3ull;
+    return (size_t)h;
+  }
+};
+
+}  // namespace
+
 struct pa_block_manager {
   int64_t nb = 0;
   int bs = 0;
-  std::deque<int32_t> free_list;
+  // Free list: FIFO of (frame, generation).  An entry is live while its frame is free and the
+  // generation matches; reviving a cached frame just marks it used (its entry goes stale).
+  std::deque<std::pair<int32_t, uint32_t>> free_list;
+  std::vector<uint32_t> free_gen;
+  std::vector<char> is_free;
+  int64_t n_free = 0;
   std::vector<int32_t> refs;  // tables referencing each frame
   struct Seq {
     std::vector<int32_t> frames;
     int64_t len = 0;  // tokens written
   };
   std::unordered_map<int64_t, Seq> seqs;
+  // Prefix tree: key -> frame; per frame its node id (-1: not registered) and key.
+  std::unordered_map<BlockKey, int32_t, BlockKeyHash> tree;
+  std::vector<int64_t> node_of;
+  std::vector<BlockKey> key_of;
+  int64_t next_node = 0;
+
+  void push_free(int32_t f) {
+    is_free[f] = 1;
+    free_list.emplace_back(f, ++free_gen[f]);
+    ++n_free;
+  }
+  void unregister(int32_t f) {
+    if (node_of[f] < 0) return;
+    tree.erase(key_of[f]);
+    key_of[f].tokens.clear();
+    node_of[f] = -1;
+  }
+  // Take the frame at the head of the free list (there must be one); a frame still registered
+  // in the prefix tree is evicted from it.
+  int32_t pop_free() {
+    for (;;) {
+      const auto e = free_list.front();
+      free_list.pop_front();
+      if (is_free[e.first] && e.second == free_gen[e.first]) {
+        is_free[e.first] = 0;
+        --n_free;
+        unregister(e.first);
+        return e.first;
+      }
+    }
+  }
+  // A registered frame referenced again (it may be waiting in the free list).
+  void revive(int32_t f) {
+    if (is_free[f]) {
+      is_free[f] = 0;
+      --n_free;
+    }
+    ++refs[f];
+  }
 };
 
 namespace {
@@ -77,7 +148,11 @@ int pa_bm_create(int64_t num_frames, int block_size, pa_block_manager** out) {
   bm->nb = num_frames;
   bm->bs = block_size;
   bm->refs.assign((size_t)num_frames, 0);
-  for (int64_t f = 0; f < num_frames; ++f) bm->free_list.push_back((int32_t)f);
+  bm->free_gen.assign((size_t)num_frames, 0);
+  bm->is_free.assign((size_t)num_frames, 0);
+  bm->node_of.assign((size_t)num_frames, -1);
+  bm->key_of.resize((size_t)num_frames);
+  for (int64_t f = 0; f < num_frames; ++f) bm->push_free((int32_t)f);
   *out = bm;
   return pa::clear_error();
 }
@@ -123,17 +198,16 @@ int pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int64_t n, int64_
     }
     ++s.len;
   }
-  if (need > (int64_t)bm->free_list.size())
-    return pa::set_error(PA_ENOSPC, "%lld free frames needed, %zu free", (long long)need,
-                         bm->free_list.size());
+  if (need > bm->n_free)
+    return pa::set_error(PA_ENOSPC, "%lld free frames needed, %lld free", (long long)need,
+                         (long long)bm->n_free);
   // Pass 2: apply.
   int64_t nc = 0;
   for (int64_t i = 0; i < n; ++i) {
     pa_block_manager::Seq& s = bm->seqs[seq_ids[i]];
     const AppendPlan p = plan_append(s, bm->bs, bm->refs);
     if (p.new_frame) {
-      const int32_t f = bm->free_list.front();
-      bm->free_list.pop_front();
+      const int32_t f = bm->pop_free();
       bm->refs[f] = 1;
       if (p.cow_from >= 0) {
         --bm->refs[p.cow_from];
@@ -168,14 +242,14 @@ int pa_bm_free(pa_block_manager* bm, int64_t seq) {
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return pa::set_error(PA_EINVAL, "unknown sequence %lld", (long long)seq);
   for (int32_t f : it->second.frames)
-    if (--bm->refs[f] == 0) bm->free_list.push_back(f);
+    if (--bm->refs[f] == 0) bm->push_free(f);
   bm->seqs.erase(it);
   return pa::clear_error();
 }
 
 int pa_bm_num_free(const pa_block_manager* bm, int64_t* out) {
   if (!bm || !out) return pa::set_error(PA_EINVAL, "null pointer argument");
-  *out = (int64_t)bm->free_list.size();
+  *out = bm->n_free;
   return pa::clear_error();
 }
 
@@ -197,11 +271,57 @@ int pa_bm_ref_count(const pa_block_manager* bm, int64_t frame, int32_t* out) {
 
 int pa_bm_free_list(const pa_block_manager* bm, int32_t* out, int64_t capacity, int64_t* count) {
   if (!bm || !count) return pa::set_error(PA_EINVAL, "null pointer argument");
-  *count = (int64_t)bm->free_list.size();
+  *count = bm->n_free;
   if (capacity < *count) return pa::set_error(PA_ERANGE, "capacity %lld < %lld free frames", (long long)capacity, (long long)*count);
   if (*count > 0 && !out) return pa::set_error(PA_EINVAL, "null output pointer");
   int64_t i = 0;
-  for (int32_t f : bm->free_list) out[i++] = f;
+  for (const auto& e : bm->free_list)
+    if (bm->is_free[e.first] && e.second == bm->free_gen[e.first]) out[i++] = e.first;
+  return pa::clear_error();
+}
+
+int pa_bm_append_prompt(pa_block_manager* bm, int64_t seq, const int32_t* tokens, int64_t n,
+                        int64_t* slots, int64_t* num_cached) {
+  if (!bm) return pa::set_error(PA_EINVAL, "null block manager");
+  if (n < 1) return pa::set_error(PA_EINVAL, "a prompt needs at least one token (n %lld)", (long long)n);
+  if (!tokens || !slots || !num_cached) return pa::set_error(PA_EINVAL, "null pointer argument");
+  if (bm->seqs.count(seq)) return pa::set_error(PA_EINVAL, "sequence %lld already exists", (long long)seq);
+  const int bs = bm->bs;
+  const int64_t full = n / bs, blocks = (n + bs - 1) / bs;
+  // match the longest run of cached full blocks
+  std::vector<int32_t> matched;
+  BlockKey key;
+  int64_t revived = 0;
+  for (int64_t k = 0; k < full; ++k) {
+    key.tokens.assign(tokens + k * bs, tokens + (k + 1) * bs);
+    const auto it = bm->tree.find(key);
+    if (it == bm->tree.end()) break;
+    matched.push_back(it->second);
+    if (bm->is_free[it->second]) ++revived;
+    key.parent = bm->node_of[it->second];
+  }
+  const int64_t need = blocks - (int64_t)matched.size();
+  if (need > bm->n_free - revived)
+    return pa::set_error(PA_ENOSPC, "%lld free frames needed, %lld free", (long long)need,
+                         (long long)(bm->n_free - revived));
+  for (int32_t f : matched) bm->revive(f);
+  pa_block_manager::Seq& s = bm->seqs[seq];
+  s.frames = matched;
+  for (int64_t k = (int64_t)matched.size(); k < blocks; ++k) {
+    const int32_t f = bm->pop_free();
+    bm->refs[f] = 1;
+    s.frames.push_back(f);
+    if (k < full) {  // a full block of this prompt: register it under its parent
+      key.tokens.assign(tokens + k * bs, tokens + (k + 1) * bs);
+      bm->tree.emplace(key, f);
+      bm->key_of[f] = key;
+      bm->node_of[f] = bm->next_node++;
+      key.parent = bm->node_of[f];
+    }
+  }
+  s.len = n;
+  for (int64_t i = 0; i < n; ++i) slots[i] = (int64_t)s.frames[i / bs] * bs + i % bs;
+  *num_cached = (int64_t)matched.size() * bs;
   return pa::clear_error();
 }
 

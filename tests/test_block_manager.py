@@ -326,3 +326,197 @@ def test_pins_pass_on_the_model():
                                     _SlotOffByOne], ids=lambda c: c.__name__)
 def test_planted_mistake_is_caught(mutant):
     assert _pins(mutant), f"no pin catches {mutant.__name__}"
+
+
+# ----------------------------------------------------------------------------- prefix caching
+#
+# Pins from codebumble.net, "CUDA Shared Memory Optimization" (a prefix tree of token blocks;
+# matching blocks are referenced, not recomputed): reuse of a shared prefix, no match once the
+# prefixes differ (the tree is keyed by the parent), partial blocks are never shared, a released
+# prefix stays findable until its frames are handed out again, and token contents stay right.
+
+
+class PromptReplay(Replay):
+    """Replay whose prompt tokens carry (token id, position): equal prefixes, equal contents."""
+
+    def prompt(self, seq, tokens, slots, cached):
+        self.history[seq] = [(int(t), p) for p, t in enumerate(tokens)]
+        for p in range(cached, len(tokens)):
+            self.cache[int(slots[p])] = self.history[seq][p]
+
+
+def _pin_prefix_reuse(cls):
+    bs = 4
+    m = cls(64, bs)
+    sys_prompt = list(range(100, 108))                    # two full blocks
+    _, c0 = m.append_prompt(0, sys_prompt + [1, 2, 3])
+    _, c1 = m.append_prompt(1, sys_prompt + [7, 8, 9, 10, 11])
+    assert (c0, c1) == (0, 8)
+    assert m.tables[1][:2] == m.tables[0][:2] and m.tables[1][2] != m.tables[0][2]
+    _, c2 = m.append_prompt(2, [5] + sys_prompt[1:] + [1])  # first block differs
+    assert c2 == 0
+    _, c3 = m.append_prompt(3, sys_prompt[:4] + [0, 0, 0, 0])  # parent matches, child differs
+    assert c3 == 4
+    _, c4 = m.append_prompt(4, sys_prompt + [1, 2, 3])     # 8 cached; the partial block is not
+    assert c4 == 8 and m.tables[4][2] != m.tables[0][2]
+    m.append_prompt(5, [50, 51, 52, 53, 60, 61, 62, 63])   # [60..63] registered under [50..53]
+    _, c6 = m.append_prompt(6, [60, 61, 62, 63])           # same tokens at another position
+    assert c6 == 0
+
+
+def _pin_prefix_release_and_eviction(cls):
+    bs = 2
+    m = cls(6, bs)
+    m.append_prompt(0, [1, 2, 3, 4])                       # frames 0, 1 registered
+    m.release(0)
+    assert m.free == [2, 3, 4, 5, 0, 1]
+    _, c = m.append_prompt(1, [1, 2, 3, 4, 9])             # revived from the free list
+    assert c == 4 and m.tables[1][:2] == [0, 1] and m.free == [3, 4, 5]
+    m.release(1)
+    assert m.free == [3, 4, 5, 0, 1, 2]
+    m.append([7] * 6)                                      # hands out 3, 4, 5
+    _, c = m.append_prompt(2, [1, 2, 3, 4])                # frames 0, 1 still registered
+    assert c == 4 and m.free == [2]
+    m.release(2)
+    m.release(7)
+    assert m.free == [2, 0, 1, 3, 4, 5]
+    m.append([8] * 10)                                     # hands out 2, 0, 1, 3, 4: evicts 0, 1
+    _, c = m.append_prompt(3, [1, 2])
+    assert c == 0 and m.tables[3] == [5]
+
+
+def _pin_prefix_content(cls):
+    rng = np.random.default_rng(9)
+    bs = 4
+    m, rep = cls(160, bs), PromptReplay(bs)
+    prompts = [list(rng.integers(0, 50, size=int(rng.integers(4, 20)))) for _ in range(3)]
+    next_id = 0
+    for _ in range(150):
+        r = rng.random()
+        live = sorted(m.tables)
+        if r < 0.3 or not live:
+            toks = prompts[int(rng.integers(0, 3))] + list(rng.integers(0, 50, size=int(rng.integers(0, 9))))
+            try:
+                slots, cached = m.append_prompt(next_id, toks)
+            except OutOfBlocks:
+                continue
+            rep.prompt(next_id, toks, slots, cached)
+            next_id += 1
+        elif r < 0.4:
+            p = int(rng.choice(live))
+            m.fork(p, next_id)
+            rep.fork(p, next_id)
+            next_id += 1
+        elif r < 0.6 and len(live) > 1:
+            s = int(rng.choice(live))
+            m.release(s)
+            rep.release(s)
+        else:
+            ids = [int(x) for x in rng.choice(live, size=int(rng.integers(1, len(live) + 1)))]
+            try:
+                slots, copies = m.append(ids)
+            except OutOfBlocks:
+                continue
+            rep.apply(ids, slots, copies)
+        rep.check(lambda s: m.tables[s])
+
+
+def test_prefix_pins_pass_on_the_model():
+    _pin_prefix_reuse(BlockManagerModel)
+    _pin_prefix_release_and_eviction(BlockManagerModel)
+    _pin_prefix_content(BlockManagerModel)
+
+
+class _KeyWithoutParent(BlockManagerModel):
+    def append_prompt(self, seq, tokens):
+        real = BlockManagerModel.append_prompt
+        saved_nodes = self.nodes
+
+        class Flat(dict):
+            def __contains__(s, key):
+                return any(k[1] == key[1] for k in dict.keys(s))
+
+            def __getitem__(s, key):
+                return next(v for k, v in dict.items(s) if k[1] == key[1])
+        self.nodes = Flat(saved_nodes)
+        try:
+            return real(self, seq, tokens)
+        finally:
+            self.nodes = dict(self.nodes)
+
+
+class _ForgetOnRelease(BlockManagerModel):
+    def release(self, seq):
+        for b in self.tables[seq]:
+            if self.users(b) == 1 and b in self.node_id:
+                del self.nodes[self.node_key.pop(b)]
+                del self.node_id[b]
+        super().release(seq)
+
+
+class _RegisterPartial(BlockManagerModel):
+    def append_prompt(self, seq, tokens):
+        pad = (-len(tokens)) % self.block_size
+        slots, cached = super().append_prompt(seq, list(tokens) + [-1] * pad)
+        self.lengths[seq] = len(tokens)
+        return slots[:len(tokens)], cached
+
+
+class _NeverEvict(BlockManagerModel):
+    def _take_free(self):
+        return self.free.pop(0)
+
+
+@pytest.mark.parametrize("mutant", [_KeyWithoutParent, _ForgetOnRelease, _RegisterPartial,
+                                    _NeverEvict], ids=lambda c: c.__name__)
+def test_prefix_planted_mistake_is_caught(mutant):
+    caught = False
+    for pin in (_pin_prefix_reuse, _pin_prefix_release_and_eviction, _pin_prefix_content):
+        try:
+            pin(mutant)
+        except (AssertionError, KeyError, StopIteration):
+            caught = True
+    assert caught, f"no pin catches {mutant.__name__}"
+
+
+@pytest.mark.parametrize("seed,bs,nb", [(21, 4, 150), (22, 16, 120), (23, 2, 80)])
+def test_library_matches_model_with_prefix_caching(seed, bs, nb):
+    rng = np.random.default_rng(seed)
+    m, bm = BlockManagerModel(nb, bs), pa.BlockManager(nb, bs)
+    prompts = [list(rng.integers(0, 40, size=int(rng.integers(bs, 5 * bs)))) for _ in range(3)]
+    next_id = 0
+    for _ in range(200):
+        live = sorted(m.tables)
+        r = rng.random()
+        if r < 0.3 or not live:
+            toks = prompts[int(rng.integers(0, 3))] + list(rng.integers(0, 40, size=int(rng.integers(0, 2 * bs))))
+            try:
+                want = m.append_prompt(next_id, toks)
+            except OutOfBlocks:
+                with pytest.raises(pa.PAError, match="ENOSPC"):
+                    bm.append_prompt(next_id, toks)
+                continue
+            slots, cached = bm.append_prompt(next_id, toks)
+            assert list(slots) == want[0] and cached == want[1]
+            next_id += 1
+        elif r < 0.4:
+            p = int(rng.choice(live))
+            m.fork(p, next_id)
+            bm.fork(p, next_id)
+            next_id += 1
+        elif r < 0.6 and len(live) > 1:
+            s = int(rng.choice(live))
+            m.release(s)
+            bm.free(s)
+        else:
+            ids = [int(x) for x in rng.choice(live, size=int(rng.integers(1, len(live) + 1)))]
+            try:
+                want = m.append(ids)
+            except OutOfBlocks:
+                with pytest.raises(pa.PAError, match="ENOSPC"):
+                    bm.append(ids)
+                continue
+            slots, copies = bm.append(ids)
+            assert list(slots) == want[0] and [tuple(c) for c in copies] == want[1]
+        _compare(bm, m, sorted(m.tables))
+    bm.close()
