@@ -18,14 +18,19 @@ namespace {
 thread_local std::string g_error;
 }  // namespace
 
-int pa::set_error(int code, const char* fmt, ...) {
+int pa::set_error_v(int code, const char* fmt, va_list ap) {
   char buf[512];
-  va_list ap;
-  va_start(ap, fmt);
   vsnprintf(buf, sizeof buf, fmt, ap);
-  va_end(ap);
   g_error = buf;
   return code;
+}
+
+int pa::set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = set_error_v(code, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 int pa::clear_error() {
@@ -35,9 +40,12 @@ int pa::clear_error() {
 
 namespace {
 
-template <typename... A>
-int fail(int code, const char* fmt, A... a) {
-  return pa::set_error(code, fmt, a...);
+__attribute__((format(printf, 2, 3))) int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  const int r = pa::set_error_v(code, fmt, ap);
+  va_end(ap);
+  return r;
 }
 
 int ok() { return pa::clear_error(); }

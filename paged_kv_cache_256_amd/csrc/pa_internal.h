@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdarg.h>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -50,6 +51,7 @@ struct PrefillParams {
 // The calling thread's error message (pa_last_error): set_error formats it and returns `code`,
 // clear_error empties it and returns PA_OK.
 int set_error(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int set_error_v(int code, const char* fmt, va_list ap);
 int clear_error();
 
 // Compute units of the current device (cached per device; 256 when no device is visible).
