@@ -213,6 +213,7 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
     return fail(PA_EINVAL, "need 1 <= max_chunk_len (%d) <= max_context_len (%d)", max_chunk_len, max_context_len);
   if (total_q > 0x7fffffff) return fail(PA_ENOTSUP, "total_q %lld too large", (long long)total_q);
   if ((long long)num_chunks * Hkv > 65535) return fail(PA_ENOTSUP, "num_chunks * Hkv too large (max 65535)");
+  if (total_q * Hq > 4LL * 0x7fffffff) return fail(PA_ENOTSUP, "total_q * Hq too large");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
     return fail(PA_EINVAL, "null pointer argument");
   const size_t need = pa::prefill_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D, (int)kv_dtype);

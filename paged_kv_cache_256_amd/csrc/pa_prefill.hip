@@ -397,13 +397,22 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
   }
 }
 
-template <int KIND>
-__global__ __launch_bounds__(128) void prefill_reduce_kernel(
+// Merge the context splits of every (row, head) whose keys span more than one split:
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.  One wavefront per
+// (row, head), four per workgroup; lane l merges head-dim elements [l*NV, (l+1)*NV).  All of a
+// row's partials are loaded before any is used.
+template <int KIND, int D>
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int num_chunks,
-    int Hq, int D, int nsplit, int KS, int cap, float v_scale) {
-  const long long r = blockIdx.x;
-  const int h = blockIdx.y;
+    long long total_q, int Hq, int nsplit, int KS, int cap, float v_scale) {
+  constexpr int NV = D / 64;       // outputs per lane
+  constexpr int kMaxSplit = 16;    // partials held in registers at once
+  const long long pair = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (pair >= total_q * Hq) return;
+  const long long r = pair / Hq;
+  const int h = (int)(pair - r * Hq);
   int lo = 0, hi = num_chunks - 1;  // last chunk c with qsl[c] <= r
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
@@ -417,22 +426,44 @@ __global__ __launch_bounds__(128) void prefill_reduce_kernel(
   const int nsp = min(nsplit, pos / KS + 1);
   if (nsp <= 1) return;
   const size_t base = ((size_t)r * Hq + h) * nsplit;
-  float M = -INFINITY;
-  for (int p = 0; p < nsp; ++p) M = fmaxf(M, ws_ml[2 * (base + p)]);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nsp; ++p) {
-      const float mp = ws_ml[2 * (base + p)];
-      if (mp == -INFINITY) continue;
-      const float e = __builtin_amdgcn_exp2f(mp - M);
-      num += e * ws_o[(base + p) * D + d];
-      den += e * ws_ml[2 * (base + p) + 1];
+  float M = -INFINITY, den = 0.f, num[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) num[v] = 0.f;
+  for (int p0 = 0; p0 < nsp; p0 += kMaxSplit) {
+    float mp[kMaxSplit], lp[kMaxSplit], op[kMaxSplit][NV];
+#pragma unroll
+    for (int i = 0; i < kMaxSplit; ++i) {
+      const bool has = p0 + i < nsp;
+      const size_t q = base + (has ? p0 + i : 0);
+      mp[i] = has ? ws_ml[2 * q] : -INFINITY;
+      lp[i] = has ? ws_ml[2 * q + 1] : 0.f;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) op[i][v] = has ? ws_o[q * D + lane * NV + v] : 0.f;
     }
-    const float o = num / den * v_scale;
+#pragma unroll
+    for (int i = 0; i < kMaxSplit; ++i) {
+      if (mp[i] == -INFINITY) continue;
+      if (mp[i] > M) {
+        const float sc = __builtin_amdgcn_exp2f(M - mp[i]);
+        den *= sc;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) num[v] *= sc;
+        M = mp[i];
+      }
+      const float e = __builtin_amdgcn_exp2f(mp[i] - M);
+      den += e * lp[i];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) num[v] += e * op[i][v];
+    }
+  }
+  const size_t o = ((size_t)r * Hq + h) * D + lane * NV;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const float x = num[v] / den * v_scale;
     if constexpr (KIND == KF32) {
-      ((float*)out)[((size_t)r * Hq + h) * D + d] = o;
+      ((float*)out)[o + v] = x;
     } else {
-      ((__bf16*)out)[((size_t)r * Hq + h) * D + d] = (__bf16)o;
+      ((__bf16*)out)[o + v] = (__bf16)x;
     }
   }
 }
@@ -475,9 +506,10 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   if (e != hipSuccess || sp.nsplit <= 1) return e;
   const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
                                                                  : p.max_blocks_per_seq * BS;
-  hipLaunchKernelGGL((prefill_reduce_kernel<KIND>), dim3((unsigned)p.total_q, p.Hq), dim3(D), 0,
-                     stream, p.out, ws_ml, ws_o, p.query_start_loc, p.context_lens,
-                     p.num_chunks, p.Hq, D, sp.nsplit, sp.KS, cap, v_scale);
+  const long long pairs = p.total_q * p.Hq;
+  hipLaunchKernelGGL((prefill_reduce_kernel<KIND, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+                     stream, p.out, ws_ml, ws_o, p.query_start_loc, p.context_lens, p.num_chunks,
+                     (long long)p.total_q, p.Hq, sp.nsplit, sp.KS, cap, v_scale);
   return hipGetLastError();
 }
 
