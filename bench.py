@@ -125,6 +125,8 @@ class DeviceState:
             self.out = torch.empty_like(self.q)
             need = pa.decode_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype, c.max_context_len)
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            # the caller's cache-policy hint: do several sequences' tables name the same frame?
+            self.shared = c.shares_frames
         if c.chunk is not None:
             ch = c.chunk
             self.cq = dv(ch.q, c.q_dtype)
@@ -157,7 +159,8 @@ class DeviceState:
         c = self.c
         self.pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, block_size=c.bs,
                        scale=c.scale, kv_dtype=c.kv_dtype, max_context_len=c.max_context_len,
-                       k_scale=c.k_scale, v_scale=c.v_scale, out=self.out, workspace=self.ws)
+                       k_scale=c.k_scale, v_scale=c.v_scale, out=self.out, workspace=self.ws,
+                       shared_frames=self.shared)
 
 
 def main():
@@ -280,7 +283,8 @@ def main():
              "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
              "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None,
-             "launch": "hip graph per phase" if args.graph else "eager"}
+             "launch": "hip graph per phase" if args.graph else "eager",
+             "decode_shared_frames_hint": bool(case.B and st.shared)}
     if case.chunk is not None:
         fl = chunk_flops(case)
         cavg = float(chunk_ms.mean())

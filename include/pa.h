@@ -149,6 +149,24 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
               pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
               int max_context_len, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_ex -- pa_decode with flags (pa_decode is pa_decode_ex with flags 0):
+ *   PA_DECODE_SHARED_FRAMES  some frames appear in the block tables of several sequences of
+ *     the batch (copy-on-write branches of one prompt, cached prefixes; bicarait.com,
+ *     "Architectural Blueprint 2"; infoisland, section 2).  K/V tiles are then read with loads
+ *     that keep them in the caches, so the sequences after the first find shared frames there;
+ *     without the flag tiles are read once each and bypass cache retention.  The flag changes
+ *     only where data is cached: results are bit-identical either way.
+ * Unknown flag bits are PA_EINVAL.
+ */
+enum { PA_DECODE_SHARED_FRAMES = 1 };
+int pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                 int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+                 pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                 int max_context_len, void* workspace, size_t workspace_bytes, unsigned flags,
+                 void* stream);
+
 /* Bytes of device workspace pa_prefill_chunk needs for these bounds (0 is a valid answer:
  * then workspace may be NULL).  The arguments are the ones pa_prefill_chunk receives. */
 size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,

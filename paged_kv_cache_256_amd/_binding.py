@@ -19,6 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
+PA_DECODE_SHARED_FRAMES = 1
 DTYPE_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -47,6 +48,8 @@ _SIGS = {
     "pa_decode_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _SZ),
     "pa_decode": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F, _F, _I,
                    _P, _SZ, _P], _I),
+    "pa_decode_ex": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F, _F, _I,
+                      _P, _SZ, ctypes.c_uint, _P], _I),
     "pa_prefill_chunk_workspace_bytes": ([_I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "pa_prefill_chunk": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I64,
                           _F, _I, _I, _F, _F, _P, _SZ, _P], _I),
@@ -160,7 +163,9 @@ def q_dtype_for(kv_dtype: str) -> str:
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, scale: float,
            kv_dtype: str, max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
-           out=None, workspace=None):
+           out=None, workspace=None, shared_frames: bool = False):
+    """pa_decode_ex; shared_frames=True when frames appear in several sequences' tables (keeps
+    them cacheable; the result is bit-identical either way)."""
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     qd = q_dtype_for(kv_dtype)
     B, Hq, Dq = q.shape
@@ -176,14 +181,14 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, 
     if os.environ.get("PA_VALIDATE") == "1":
         validate_decode_indices(block_tables.cpu().numpy(), context_lens.cpu().numpy(),
                                 block_size, NB, max_context_len)
-    _check(_lib.pa_decode(_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
-                          _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
-                          _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
-                          _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
-                          _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D,
-                          block_size, NB, float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype],
-                          float(k_scale), float(v_scale), int(max_context_len), ws, wsb,
-                          _stream(q)))
+    _check(_lib.pa_decode_ex(_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+                             _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+                             _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+                             _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+                             _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D,
+                             block_size, NB, float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype],
+                             float(k_scale), float(v_scale), int(max_context_len), ws, wsb,
+                             PA_DECODE_SHARED_FRAMES if shared_frames else 0, _stream(q)))
     return out
 
 

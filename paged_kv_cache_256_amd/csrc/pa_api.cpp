@@ -158,11 +158,12 @@ size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype 
   return pa::decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len);
 }
 
-int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+int pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
               int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
               pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
-              int max_context_len, void* workspace, size_t workspace_bytes, void* stream) {
+              int max_context_len, void* workspace, size_t workspace_bytes, unsigned flags,
+                 void* stream) {
   if (B < 0 || NB < 1 || max_blocks_per_seq < 1)
     return fail(PA_EINVAL, "bad sizes (B %d, NB %lld, max_blocks_per_seq %d)", B, (long long)NB, max_blocks_per_seq);
   if (B > 65535) return fail(PA_ENOTSUP, "batch %d too large for one call (max 65535)", B);
@@ -171,6 +172,7 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
   if (int r = check_attn_dtypes(q_dtype, kv_dtype)) return r;
   if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
   if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (flags & ~(unsigned)PA_DECODE_SHARED_FRAMES) return fail(PA_EINVAL, "unknown decode flags 0x%x", flags);
   if (B == 0) return ok();
   if (max_context_len < 1) return fail(PA_EINVAL, "max_context_len %d must be positive", max_context_len);
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
@@ -180,8 +182,19 @@ int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
   pa::DecodeParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      B, Hq, Hkv, D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
-                     max_context_len, need > 0 ? workspace : nullptr};
+                     max_context_len, need > 0 ? workspace : nullptr,
+                     (flags & PA_DECODE_SHARED_FRAMES) != 0};
   return hip_status(pa::launch_decode(p, (hipStream_t)stream), "decode launch");
+}
+
+int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+              int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+              pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+              int max_context_len, void* workspace, size_t workspace_bytes, void* stream) {
+  return pa_decode_ex(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B,
+                      Hq, Hkv, D, block_size, NB, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                      max_context_len, workspace, workspace_bytes, 0u, stream);
 }
 
 size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,

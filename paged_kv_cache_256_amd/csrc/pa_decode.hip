@@ -55,16 +55,16 @@ constexpr int kIds = 64;     // block ids fetched per vector load
 constexpr int kRestart = PA_DECODE_RESTART_UNITS;
 __host__ __device__ inline int run_units(int nblk) { return nblk > 0 ? nblk + kRestart : 0; }
 
-// Tile loads bypass cache retention by default (each tile is read once per step).
-#ifndef PA_DECODE_NONTEMPORAL
-#define PA_DECODE_NONTEMPORAL 1
-#endif
+// Tile loads: non-temporal (not retained in the caches) when every frame is read once per call;
+// ordinary loads when frames are shared between sequences of the batch (copy-on-write branches,
+// cached prefixes), so that the sequences after the first find them in L2 / the MALL.
+template <bool NONTEMPORAL>
 __device__ inline u32x4 load_tile16(const u32x4* p) {
-#if PA_DECODE_NONTEMPORAL
-  return __builtin_nontemporal_load(p);
-#else
-  return *p;
-#endif
+  if constexpr (NONTEMPORAL) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
 }
 
 // Frames per pipeline step: two when a tile is 4 KiB or less (double-buffered K+V of two frames
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
 
 __device__ inline long long range_begin(long long F, int w, int W) { return F * w / W; }
 
-template <int KIND, int D, int BS, int F>
+template <int KIND, int D, int BS, int F, bool NT>
 __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
@@ -263,9 +263,9 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
       const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
       const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
 #pragma unroll
-      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16(kp + r * 64);
+      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16<NT>(kp + r * 64);
 #pragma unroll
-      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16(vp + r * 64);
+      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16<NT>(vp + r * 64);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -551,8 +551,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((decode_stream_kernel<KIND, D, BS, F>), dim3(l.W / kWaves), dim3(kWaves * 64),
-                     0, stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
+  auto stream_kernel = p.shared_frames ? decode_stream_kernel<KIND, D, BS, F, false>
+                                       : decode_stream_kernel<KIND, D, BS, F, true>;
+  hipLaunchKernelGGL(stream_kernel, dim3(l.W / kWaves), dim3(kWaves * 64), 0, stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
                      p.block_tables, p.context_lens, plan, inline_plan, ws_ml, ws_o, p.B,
                      p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale);
   e = hipGetLastError();

@@ -26,6 +26,7 @@ struct DecodeParams {
   float k_scale, v_scale;
   int max_context_len;
   void* workspace;
+  bool shared_frames;  // frames referenced by several sequences: keep them cacheable
 };
 
 struct PrefillParams {

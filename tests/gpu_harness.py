@@ -90,7 +90,8 @@ class GpuStep:
         self.out = pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, block_size=c.bs,
                              scale=c.scale, kv_dtype=c.kv_dtype,
                              max_context_len=kw.pop("max_context_len", c.max_context_len),
-                             k_scale=c.k_scale, v_scale=c.v_scale, **kw)
+                             k_scale=c.k_scale, v_scale=c.v_scale,
+                             shared_frames=kw.pop("shared_frames", c.shares_frames), **kw)
         return self.out
 
     def step(self):

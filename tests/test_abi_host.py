@@ -249,3 +249,13 @@ def test_validate_chunk_indices():
     with pytest.raises(pa.PAError, match="decreases"):
         pa.validate_chunk_indices(bt, np.array([0, 10, 5], np.int32), np.array([40, 20], np.int32),
                                   16, 6, 20, 48)
+
+
+def test_decode_ex_rejects_unknown_flags():
+    f = lib().pa_decode_ex
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 8, 2, 128, 16, 64, 0.1, BF16, BF16, 1.0, 1.0,
+            128, FAKE, 1 << 40]
+    assert f(*args, 2, NULL) == EINVAL and "unknown decode flags" in err()
+    assert f(*args, 1 << 31, NULL) == EINVAL
+    # flag 1 (shared frames) is accepted: the call then fails only on the fake workspace size
+    assert f(*(args[:-1] + [0]), 1, NULL) == ENOSPC

@@ -347,3 +347,24 @@ def test_graph_replays_match_eager_bits():
     o = OracleStep(c)
     err = np.abs(out_f64(out) - o.decode()).max()
     assert err <= tolerance(c)
+
+
+@pytest.mark.parametrize("shared", ["fork", "plain"])
+def test_shared_frames_hint_gives_identical_bits(shared):
+    """The cache-policy flag changes only where tiles are cached: both settings, bit for bit."""
+    _say(f"shared-frames hint, {shared} case")
+    if shared == "fork":
+        c = workloads.fork_case("hint-fork", 5, prompts=4, branches=4, prompt_len=256, tail_lo=1,
+                                tail_hi=100, Hq=32, Hkv=4, D=128, bs=32, kv_dtype="fp8")
+    else:
+        c = workloads.decode_case("hint-plain", 5, Hq=16, Hkv=2, D=128, bs=16,
+                                  lens=[1, 100, 1000, 3000], kv_dtype="bf16", std=0.7071)
+    g = GpuStep(c)
+    g.write()
+    a = g.decode(shared_frames=False).clone()
+    b = g.decode(shared_frames=True).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert c.shares_frames == (shared == "fork")
+    o = OracleStep(c)
+    assert np.abs(out_f64(b) - o.decode()).max() <= tolerance(c)

@@ -145,6 +145,16 @@ class DecodeCase:
     def kv_elem_bytes(self) -> int:
         return {"f32": 4, "bf16": 2, "fp8": 1}[self.kv_dtype]
 
+    @property
+    def shares_frames(self) -> bool:
+        """True if some frame appears in the used block-table entries of two decode sequences
+        (the caller's hint that frames are shared within the batch)."""
+        if not self.B:
+            return False
+        nblk = (self.context_lens.astype(np.int64) + self.bs - 1) // self.bs
+        used = np.concatenate([self.block_tables[b, :n] for b, n in enumerate(nblk)])
+        return bool(np.unique(used).size < used.size)
+
     def decode_kv_bytes(self, seqs=None) -> int:
         """Algorithmic KV bytes a decode step must read: L * 2 * Hkv * D * b per sequence."""
         lens = self.context_lens if seqs is None else self.context_lens[seqs]
