@@ -139,6 +139,40 @@ class DeviceState:
                 c.Hkv, c.D, c.bs, c.kv_dtype)
             self.cws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
 
+    def init_mixed(self, dev, mode="auto"):
+        """Inputs of pa_mixed_attention: the decodes and the chunks as one batch (decodes first)."""
+        import torch
+
+        import workloads
+
+        c, pa = self.c, self.pa
+        m = self.m = workloads.mixed_batch(c)
+        self.mq = (torch.from_numpy(np.ascontiguousarray(m.q).view(np.int16)).to(dev).view(torch.bfloat16)
+                   if c.q_dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(m.q)).to(dev))
+        self.mtables = torch.from_numpy(m.block_tables).to(dev)
+        self.mqsl = torch.from_numpy(m.query_start_loc).to(dev)
+        self.mlens = torch.from_numpy(m.context_lens).to(dev)
+        self.mout = torch.empty_like(self.mq)
+        need = pa.mixed_workspace_bytes(m.num_decodes, c.chunk.num_chunks, self.mq.shape[0],
+                                        m.max_chunk_len, m.max_context_len, c.Hq, c.Hkv, c.D,
+                                        c.bs, c.kv_dtype)
+        self.mws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        self.mixed_units = pa.mixed_prefill_units(m.num_decodes, c.chunk.num_chunks,
+                                                  self.mq.shape[0], m.max_chunk_len,
+                                                  m.max_context_len, m.decode_tokens, c.Hq, c.Hkv,
+                                                  c.D, c.bs, c.kv_dtype, mode)
+        self.mixed_mode = mode
+
+    def mixed(self):
+        c, m = self.c, self.m
+        self.pa.mixed_attention(self.mq, self.kc, self.vc, self.mtables, self.mqsl, self.mlens,
+                                m.num_decodes, block_size=c.bs, scale=c.scale,
+                                kv_dtype=c.kv_dtype, max_chunk_len=m.max_chunk_len,
+                                max_context_len=m.max_context_len, decode_tokens=m.decode_tokens,
+                                k_scale=c.k_scale, v_scale=c.v_scale, out=self.mout,
+                                workspace=self.mws, shared_frames=self.shared,
+                                mode=self.mixed_mode)
+
     def write(self):
         c, pa = self.c, self.pa
         if self.pairs is not None:
@@ -176,6 +210,11 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="capture each phase of the step in a HIP graph and replay the graphs "
                          "(default: launch every call from Python each step)")
+    ap.add_argument("--mixed", action="store_true",
+                    help="run the step's chunks and decodes in one pa_mixed_attention call "
+                         "(workloads with both)")
+    ap.add_argument("--mixed-mode", default="auto", choices=["auto", "split", "separate"],
+                    help="launch mode of pa_mixed_attention (auto: the library's choice)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run three plain device copies of this many MiB before the timed steps "
                          "(a known-size reference for hardware byte counters)")
@@ -209,8 +248,15 @@ def main():
         del src, dst
 
     # the three phases of a step; each is one call of the library
-    phases = [st.write, st.prefill if case.chunk is not None else None,
-              st.decode if case.B else None]
+    if args.mixed:
+        if case.chunk is None or not case.B:
+            print("bench.py: --mixed needs a workload with chunks and decodes", file=sys.stderr)
+            sys.exit(2)
+        st.init_mixed(dev, args.mixed_mode)
+        phases = [st.write, st.mixed, None]
+    else:
+        phases = [st.write, st.prefill if case.chunk is not None else None,
+                  st.decode if case.B else None]
     if args.graph:
         # one HIP graph per phase: a step replays the three graphs, so no host time sits
         # between the kernels of a phase
@@ -267,7 +313,7 @@ def main():
     value = kv_bytes / (ms * 1e-3) / 1e9 if case.B else 0.0
     seqs_per_s = case.B / (ms * 1e-3)
     dec_avg = float(dec_ms.mean())
-    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9 if case.B else 0.0
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9 if case.B and dec_avg > 0 else 0.0
     traffic = measured_traffic(case.name) if case.B else None
     kernels = ("decode_stream_kernel + decode_reduce_kernel" if case.B <= 1024 else
                "decode_plan_kernel + decode_stream_kernel + decode_reduce_kernel")
@@ -284,8 +330,32 @@ def main():
                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
              "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None,
              "launch": "hip graph per phase" if args.graph else "eager",
+             "attention_calls": "pa_mixed_attention" if args.mixed else
+                                "pa_prefill_chunk + pa_decode" if case.chunk is not None and case.B else
+                                "pa_prefill_chunk" if case.chunk is not None else "pa_decode",
              "decode_shared_frames_hint": bool(case.B and st.shared)}
-    if case.chunk is not None:
+    if args.mixed:
+        fl = chunk_flops(case)
+        mavg = float(chunk_ms.mean())
+        achieved = kv_bytes / (mavg * 1e-3) / 1e9
+        extra.pop("decode_us")
+        extra.pop("decode_us_p10_p90")
+        extra["mixed_us"] = round(mavg * 1e3, 2)
+        extra["mixed_us_p10_p90"] = [round(float(np.percentile(chunk_ms, 10)) * 1e3, 2),
+                                     round(float(np.percentile(chunk_ms, 90)) * 1e3, 2)]
+        extra["mixed_prefill_units"] = st.mixed_units
+        extra["mixed_mode"] = args.mixed_mode
+        extra["chunk_flop"] = fl
+        extra["mixed_chunk_tflops"] = round(fl / (mavg * 1e-3) / 1e12, 2)
+        extra["mixed_chunk_frac_of_mfma_bf16_peak"] = round(fl / (mavg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "mixed_kernel + mixed_merge_kernel (one pa_mixed_attention call: "
+                              "decode KV bytes over the whole launch, which also runs the chunk)",
+                    "avg_us": extra["mixed_us"], "algorithmic_bytes_per_launch": kv_bytes,
+                    "traffic_source": None}
+        dec_avg = mavg
+    elif case.chunk is not None:
         fl = chunk_flops(case)
         cavg = float(chunk_ms.mean())
         extra["chunk_us"] = round(cavg * 1e3, 2)

@@ -198,6 +198,75 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
                      size_t workspace_bytes, void* stream);
 
 /*
+ * Bytes of device workspace pa_mixed_attention needs for these bounds (0 is a valid answer:
+ * then workspace may be NULL).  It holds the decode plan and partials (sized, as for
+ * pa_decode, by the device's compute units) and the chunk rows' split partials.
+ */
+size_t pa_mixed_workspace_bytes(int num_decodes, int num_chunks, int64_t total_q,
+                                int max_chunk_len, int max_context_len, int Hq, int Hkv, int D,
+                                int block_size, pa_dtype kv_dtype);
+
+/*
+ * pa_mixed_attention -- one step of a mixed batch in one attention kernel: prefill chunks
+ * paired with the ongoing decodes in the same GPU iteration (bicarait.com, "Architectural
+ * Blueprint 3"; infoisland, section 5).  The batch has num_decodes + num_chunks sequences,
+ * decodes first:
+ *   sequence b < num_decodes      a decode: query row b (query_start_loc[b] = b); out[b] is
+ *                                 pa_decode's result for q[b], block_tables[b], context_lens[b].
+ *   sequence s = num_decodes + c  chunk c: rows [query_start_loc[s], query_start_loc[s+1]);
+ *                                 out rows are pa_prefill_chunk's result for that chunk.
+ *   out, q           [total_q, Hq, D] in q_dtype, contiguous;
+ *                    total_q = query_start_loc[num_decodes + num_chunks].
+ *   block_tables     int32 [num_decodes + num_chunks, max_blocks_per_seq].
+ *   query_start_loc  int32 [num_decodes + num_chunks + 1], query_start_loc[b] = b for
+ *                    b <= num_decodes, non-decreasing after.
+ *   context_lens     int32 [num_decodes + num_chunks], each in [1, max_context_len]; a
+ *                    chunk's length is at least its row count.
+ *   max_chunk_len    host-side bound on the chunks' row counts (ignored when num_chunks = 0).
+ *   decode_tokens    the sum of the decodes' context lengths as the host knows it (a block
+ *                    manager does), or <= 0 if unknown.  It only decides how many compute
+ *                    units take each half; the results do not depend on it.
+ *   flags            PA_DECODE_SHARED_FRAMES as for pa_decode_ex (decode loads only);
+ *                    PA_MIXED_SPLIT or PA_MIXED_SEPARATE force the mode (below) instead of
+ *                    the host's choice (for tuning and tests; results agree either way).
+ *   workspace        at least pa_mixed_workspace_bytes(...) bytes; concurrent calls must not
+ *                    share one.
+ * Every K/V the step attends (the chunks' own rows and the decodes' new tokens) must already be
+ * in the cache (pa_reshape_and_cache on the same stream).  Outputs match pa_decode and
+ * pa_prefill_chunk to fp32 rounding (the context splits differ); equal inputs and decode_tokens
+ * give equal output bits.  Argument errors are those of the two calls.  The kernels read
+ * query_start_loc only for the chunks; pa_validate_mixed_indices checks the whole batch on the
+ * host.
+ * Modes, picked on the host from the sizes and decode_tokens:
+ *   split     one persistent attention kernel with one workgroup per compute unit: some run
+ *             prefill tiles while the others stream the decodes, so the matrix cores and HBM
+ *             work at once; then one kernel merges the split partials of both halves (above
+ *             1024 decodes a one-workgroup plan kernel runs first).
+ *   separate  the pa_prefill_chunk kernels on the chunks, then the pa_decode kernels.
+ * The split is taken when the decodes' bytes are small next to the chunks' matrix work, where it
+ * is predicted to be faster.
+ */
+enum { PA_MIXED_SPLIT = 2, PA_MIXED_SEPARATE = 4 };
+int pa_mixed_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* query_start_loc, const int32_t* context_lens,
+                       int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                       int max_context_len, int64_t decode_tokens, int Hq, int Hkv, int D,
+                       int block_size, int64_t NB, float scale, pa_dtype q_dtype,
+                       pa_dtype kv_dtype, float k_scale, float v_scale, void* workspace,
+                       size_t workspace_bytes, unsigned flags, void* stream);
+
+/*
+ * How a pa_mixed_attention call with these arguments (and flags) uses the device: the number of
+ * workgroups (one per compute unit) that run prefill tiles while the others stream the decodes
+ * from the start (split mode).  The device's compute-unit count means the separate mode (or
+ * chunks only), 0 means decodes only.  -1 on invalid arguments.
+ */
+int pa_mixed_prefill_units(int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                           int max_context_len, int64_t decode_tokens, int Hq, int Hkv, int D,
+                           int block_size, pa_dtype kv_dtype, unsigned flags);
+
+/*
  * Host-side validators (no GPU needed).  Each returns PA_OK or PA_EINVAL/PA_ERANGE with
  * pa_last_error() naming the first offending entry.
  *  pa_validate_decode_indices: 1 <= context_lens[b] <= min(max_context_len,
@@ -211,6 +280,9 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
  *    chunk length is at most max_chunk_len and at most its context length, context
  *    lengths are in [1, max_context_len], and the table entries the context covers are
  *    in [0, NB).
+ *  pa_validate_mixed_indices: the decode rules for sequences [0, num_decodes), with
+ *    query_start_loc[b] = b for b <= num_decodes, and the chunk rules (query rows counted
+ *    from query_start_loc[num_decodes]) for the num_chunks sequences after them.
  */
 int pa_validate_decode_indices(const int32_t* block_tables, int max_blocks_per_seq,
                                const int32_t* context_lens, int B, int block_size, int64_t NB,
@@ -221,6 +293,10 @@ int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_se
                               const int32_t* query_start_loc, const int32_t* context_lens,
                               int num_chunks, int block_size, int64_t NB, int max_chunk_len,
                               int max_context_len);
+int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int num_decodes, int num_chunks, int block_size, int64_t NB,
+                              int max_chunk_len, int max_context_len);
 
 /*
  * Host-side block manager (no GPU involved): the bookkeeping that produces the block tables,

@@ -47,6 +47,7 @@ from .paged_attention import (  # noqa: F401
     gather_kv,
     decode,
     prefill_chunk,
+    mixed_attention,
     slot_of,
 )
 from .block_manager import BlockManagerModel, OutOfBlocks  # noqa: F401

@@ -195,3 +195,23 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_le
                 out[r, g * G:(g + 1) * G] = _softmax_attend(
                     qr[g * G:(g + 1) * G], K[:pos + 1, g], V[:pos + 1, g], scale)
     return out
+
+
+def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                    num_decodes: int, *, scale: float, bs: int, q_dtype: str, kv_dtype: str,
+                    k_scale: float = 1.0, v_scale: float = 1.0, rows=None) -> np.ndarray:
+    """One step of a mixed batch: a prefill chunk and the ongoing decodes in the same iteration
+    (bicarait.com, "Architectural Blueprint 3"; infoisland, section 5).  Sequences
+    [0, num_decodes) are decodes, each with the single query row b (query_start_loc[b] = b); the
+    others are chunks as in prefill_chunk.  A decode is its one query against its whole context,
+    which is a chunk of one row at position L - 1, so the step is prefill_chunk over every
+    sequence of the batch.  Returns float64 [total_q, Hq, D].
+
+    parity: pinned (decode rows equal decode() on the decodes alone, chunk rows equal
+    prefill_chunk() on the chunks alone)."""
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    if num_decodes < 0 or np.any(qsl[:num_decodes + 1] != np.arange(num_decodes + 1)):
+        raise ValueError("decode b must own query row b")
+    return prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                         scale=scale, bs=bs, q_dtype=q_dtype, kv_dtype=kv_dtype, k_scale=k_scale,
+                         v_scale=v_scale, rows=rows)

@@ -7,6 +7,7 @@ declared in include/pa.h:
     copy_blocks        duplicate frames for copy-on-write
     decode             paged GQA decode attention (split over the context + reduce)
     prefill_chunk      causal attention of prefill chunks over their paged context
+    mixed_attention    decodes and prefill chunks of one step in one persistent kernel
     BlockManager       host-side frames, block tables, slots and copy-on-write pairs
 """
 
@@ -21,6 +22,9 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     last_error,
     lib,
+    mixed_attention,
+    mixed_prefill_units,
+    mixed_workspace_bytes,
     new_kv_cache,
     prefill_chunk,
     prefill_chunk_workspace_bytes,
@@ -29,5 +33,6 @@ from ._binding import (  # noqa: F401
     validate_chunk_indices,
     validate_copy_pairs,
     validate_decode_indices,
+    validate_mixed_indices,
     validate_slots,
 )

@@ -20,6 +20,8 @@ LIB_PATH = os.path.join(_HERE, "libpa.so")
 
 PA_F32, PA_BF16, PA_FP8_E4M3 = 0, 1, 2
 PA_DECODE_SHARED_FRAMES = 1
+PA_MIXED_SPLIT = 2
+PA_MIXED_SEPARATE = 4
 DTYPE_CODE = {"f32": PA_F32, "bf16": PA_BF16, "fp8": PA_FP8_E4M3}
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -53,10 +55,15 @@ _SIGS = {
     "pa_prefill_chunk_workspace_bytes": ([_I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "pa_prefill_chunk": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I64,
                           _F, _I, _I, _F, _F, _P, _SZ, _P], _I),
+    "pa_mixed_workspace_bytes": ([_I, _I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
+    "pa_mixed_attention": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I64, _I, _I, _I64, _I, _I,
+                            _I, _I, _I64, _F, _I, _I, _F, _F, _P, _SZ, ctypes.c_uint, _P], _I),
+    "pa_mixed_prefill_units": ([_I, _I, _I64, _I, _I, _I64, _I, _I, _I, _I, _I, ctypes.c_uint], _I),
     "pa_validate_decode_indices": ([_P, _I, _P, _I, _I, _I64, _I], _I),
     "pa_validate_slots": ([_P, _I64, _I64, _I], _I),
     "pa_validate_copy_pairs": ([_P, _I64, _I64], _I),
     "pa_validate_chunk_indices": ([_P, _I, _P, _P, _I, _I, _I64, _I, _I], _I),
+    "pa_validate_mixed_indices": ([_P, _I, _P, _P, _I, _I, _I, _I64, _I, _I], _I),
     "pa_bm_create": ([_I64, _I, _P], _I),
     "pa_bm_destroy": ([_P], None),
     "pa_bm_append": ([_P, _P, _I64, _P, _P, _P], _I),
@@ -232,6 +239,73 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_le
     return out
 
 
+def mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len, Hq,
+                          Hkv, D, block_size, kv_dtype) -> int:
+    return int(_lib.pa_mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len,
+                                              max_context_len, Hq, Hkv, D, block_size,
+                                              DTYPE_CODE[kv_dtype]))
+
+
+def _mixed_flags(shared_frames: bool, mode: str) -> int:
+    modes = {"auto": 0, "split": PA_MIXED_SPLIT, "separate": PA_MIXED_SEPARATE}
+    if mode not in modes:
+        raise ValueError(f"mode must be one of {sorted(modes)}")
+    return (PA_DECODE_SHARED_FRAMES if shared_frames else 0) | modes[mode]
+
+
+def mixed_prefill_units(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len,
+                        decode_tokens, Hq, Hkv, D, block_size, kv_dtype, mode: str = "auto") -> int:
+    """Workgroups a pa_mixed_attention call with these sizes runs prefill tiles on while the
+    others stream the decodes (the CU count: separate kernels, or chunks only; 0: decodes only)."""
+    return int(_lib.pa_mixed_prefill_units(num_decodes, num_chunks, total_q, max_chunk_len,
+                                           max_context_len, int(decode_tokens), Hq, Hkv, D,
+                                           block_size, DTYPE_CODE[kv_dtype],
+                                           _mixed_flags(False, mode)))
+
+
+def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                    num_decodes: int, *, block_size: int, scale: float, kv_dtype: str,
+                    max_chunk_len: int, max_context_len: int, decode_tokens: int = 0,
+                    k_scale: float = 1.0, v_scale: float = 1.0, out=None, workspace=None,
+                    shared_frames: bool = False, mode: str = "auto"):
+    """pa_mixed_attention: the first num_decodes sequences are decodes (query row b), the rest
+    prefill chunks; one kernel runs both.  decode_tokens (sum of the decodes' context lengths,
+    known on the host) and mode ("auto", "split": one kernel runs both halves side by side,
+    "separate": the chunk kernels then the decode kernels) only decide how the call uses the
+    device."""
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    qd = q_dtype_for(kv_dtype)
+    total_q, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    num_chunks = context_lens.shape[0] - int(num_decodes)
+    if num_chunks < 0 or query_start_loc.shape[0] != context_lens.shape[0] + 1:
+        raise ValueError("query_start_loc must have one entry more than context_lens, which "
+                         "covers the decodes and the chunks")
+    if out is None:
+        out = torch.empty_like(q)
+    need = mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len,
+                                 Hq, Hkv, D, block_size, kv_dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if os.environ.get("PA_VALIDATE") == "1":
+        validate_mixed_indices(block_tables.cpu().numpy(), query_start_loc.cpu().numpy(),
+                               context_lens.cpu().numpy(), num_decodes, block_size, NB,
+                               max_chunk_len, max_context_len)
+    _check(_lib.pa_mixed_attention(
+        _dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+        _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]), _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(query_start_loc, "query_start_loc", torch.int32, 1),
+        _dev(context_lens, "context_lens", torch.int32, 1), int(num_decodes), num_chunks, total_q,
+        int(max_chunk_len), int(max_context_len), int(decode_tokens), Hq, Hkv, D, block_size, NB,
+        float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), ws,
+        wsb, _mixed_flags(shared_frames, mode), _stream(q)))
+    return out
+
+
 # ----------------------------------------------------------------------------- host validators
 
 
@@ -264,6 +338,19 @@ def validate_chunk_indices(block_tables, query_start_loc, context_lens, block_si
     cl, pcl = _host(context_lens, np.int32)
     _check(_lib.pa_validate_chunk_indices(pbt, bt.shape[1], pqs, pcl, cl.shape[0], block_size, NB,
                                           int(max_chunk_len), int(max_context_len)))
+
+
+def validate_mixed_indices(block_tables, query_start_loc, context_lens, num_decodes, block_size,
+                           NB, max_chunk_len, max_context_len):
+    bt, pbt = _host(block_tables, np.int32)
+    qs, pqs = _host(query_start_loc, np.int32)
+    cl, pcl = _host(context_lens, np.int32)
+    nd = int(num_decodes)
+    if not 0 <= nd <= cl.shape[0] or qs.shape[0] != cl.shape[0] + 1 or bt.shape[0] != cl.shape[0]:
+        raise ValueError("inconsistent mixed-batch index shapes")
+    _check(_lib.pa_validate_mixed_indices(pbt, bt.shape[1], pqs, pcl, nd, cl.shape[0] - nd,
+                                          block_size, NB, int(max_chunk_len),
+                                          int(max_context_len)))
 
 
 # ----------------------------------------------------------------------------- block manager

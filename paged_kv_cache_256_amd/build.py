@@ -22,7 +22,8 @@ OUT_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libpa.so")
 ARCH = "gfx950"
 
-SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_cache.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.cpp", "pa_block_manager.cpp", "pa_cache.hip", "pa_decode.hip", "pa_mixed.hip",
+           "pa_prefill.hip"]
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -9,7 +9,6 @@
 #include <cstdio>
 #include <string>
 #include <unordered_set>
-#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -235,8 +234,122 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   pa::PrefillParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, query_start_loc,
                       context_lens, num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,
                       D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
-                      need > 0 ? workspace : nullptr};
+                      need > 0 ? workspace : nullptr, 0};
   return hip_status(pa::launch_prefill(p, (hipStream_t)stream), "prefill_chunk launch");
+}
+
+// Size and shape checks shared by the mixed-batch calls.
+static int check_mixed(int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                       int max_context_len, int Hq, int Hkv, int D, int block_size,
+                       pa_dtype kv_dtype) {
+  if (num_decodes < 0 || num_chunks < 0 || total_q < num_decodes)
+    return fail(PA_EINVAL, "bad sizes (num_decodes %d, num_chunks %d, total_q %lld)", num_decodes,
+                num_chunks, (long long)total_q);
+  if (num_decodes > 65535) return fail(PA_ENOTSUP, "%d decodes too many for one call (max 65535)", num_decodes);
+  if (int r = check_heads(Hq, Hkv)) return r;
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (max_context_len < 1) return fail(PA_EINVAL, "max_context_len %d must be positive", max_context_len);
+  if (num_chunks > 0 && total_q > num_decodes &&
+      (max_chunk_len < 1 || max_context_len < max_chunk_len))
+    return fail(PA_EINVAL, "need 1 <= max_chunk_len (%d) <= max_context_len (%d)", max_chunk_len, max_context_len);
+  if (total_q > 0x7fffffff) return fail(PA_ENOTSUP, "total_q %lld too large", (long long)total_q);
+  if ((long long)num_chunks * Hkv > 65535) return fail(PA_ENOTSUP, "num_chunks * Hkv too large (max 65535)");
+  if (total_q * Hq > 4LL * 0x7fffffff) return fail(PA_ENOTSUP, "total_q * Hq too large");
+  return PA_OK;
+}
+
+static pa::MixedParams mixed_params(int num_decodes, int num_chunks, int64_t total_q,
+                                    int max_chunk_len, int max_context_len, int64_t decode_tokens,
+                                    int Hq, int Hkv, int D, int block_size, pa_dtype kv_dtype) {
+  pa::MixedParams p{};
+  p.num_decodes = num_decodes;
+  p.num_chunks = num_chunks;
+  p.total_q = total_q;
+  p.max_chunk_len = max_chunk_len;
+  p.max_context_len = max_context_len;
+  p.decode_tokens = decode_tokens;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.bs = block_size;
+  p.kv_dtype = (int)kv_dtype;
+  return p;
+}
+
+size_t pa_mixed_workspace_bytes(int num_decodes, int num_chunks, int64_t total_q,
+                                int max_chunk_len, int max_context_len, int Hq, int Hkv, int D,
+                                int block_size, pa_dtype kv_dtype) {
+  if (check_mixed(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D,
+                  block_size, kv_dtype) != PA_OK)
+    return 0;
+  return pa::mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len,
+                                   max_context_len, Hq, Hkv, D, (int)kv_dtype);
+}
+
+static int mixed_mode(unsigned flags) {
+  return (flags & PA_MIXED_SPLIT) ? pa::MIXED_SPLIT
+                                  : ((flags & PA_MIXED_SEPARATE) ? pa::MIXED_SEPARATE : pa::MIXED_AUTO);
+}
+
+int pa_mixed_prefill_units(int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                           int max_context_len, int64_t decode_tokens, int Hq, int Hkv, int D,
+                           int block_size, pa_dtype kv_dtype, unsigned flags) {
+  if (check_mixed(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D,
+                  block_size, kv_dtype) != PA_OK)
+    return -1;
+  if ((flags & PA_MIXED_SPLIT) && (flags & PA_MIXED_SEPARATE)) return -1;
+  pa::MixedParams p = mixed_params(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len,
+                                   decode_tokens, Hq, Hkv, D, block_size, kv_dtype);
+  p.mode = mixed_mode(flags);
+  return pa::mixed_prefill_workgroups(p);
+}
+
+int pa_mixed_attention(void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int max_blocks_per_seq,
+                       const int32_t* query_start_loc, const int32_t* context_lens,
+                       int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                       int max_context_len, int64_t decode_tokens, int Hq, int Hkv, int D,
+                       int block_size, int64_t NB, float scale, pa_dtype q_dtype,
+                       pa_dtype kv_dtype, float k_scale, float v_scale, void* workspace,
+                       size_t workspace_bytes, unsigned flags, void* stream) {
+  if (NB < 1 || max_blocks_per_seq < 1)
+    return fail(PA_EINVAL, "bad sizes (NB %lld, max_blocks_per_seq %d)", (long long)NB, max_blocks_per_seq);
+  if (int r = check_mixed(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len, Hq,
+                          Hkv, D, block_size, kv_dtype))
+    return r;
+  if (int r = check_attn_dtypes(q_dtype, kv_dtype)) return r;
+  if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (flags & ~(unsigned)(PA_DECODE_SHARED_FRAMES | PA_MIXED_SPLIT | PA_MIXED_SEPARATE))
+    return fail(PA_EINVAL, "unknown flags 0x%x", flags);
+  if ((flags & PA_MIXED_SPLIT) && (flags & PA_MIXED_SEPARATE))
+    return fail(PA_EINVAL, "PA_MIXED_SPLIT and PA_MIXED_SEPARATE exclude each other");
+  if (num_decodes == 0 && (num_chunks == 0 || total_q == 0)) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens ||
+      (num_chunks > 0 && !query_start_loc))
+    return fail(PA_EINVAL, "null pointer argument");
+  const size_t need = pa::mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len,
+                                                max_context_len, Hq, Hkv, D, (int)kv_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  pa::MixedParams p = mixed_params(num_decodes, num_chunks, total_q, max_chunk_len,
+                                   max_context_len, decode_tokens, Hq, Hkv, D, block_size, kv_dtype);
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.query_start_loc = query_start_loc;
+  p.context_lens = context_lens;
+  p.NB = NB;
+  p.scale = scale;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.workspace = need > 0 ? workspace : nullptr;
+  p.shared_frames = (flags & PA_DECODE_SHARED_FRAMES) != 0;
+  p.mode = mixed_mode(flags);
+  return hip_status(pa::launch_mixed(p, (hipStream_t)stream), "mixed_attention launch");
 }
 
 // ----------------------------------------------------------------------------- validators
@@ -294,16 +407,16 @@ int pa_validate_copy_pairs(const int64_t* pairs, int64_t N, int64_t NB) {
   return ok();
 }
 
-int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_seq,
-                              const int32_t* query_start_loc, const int32_t* context_lens,
-                              int num_chunks, int block_size, int64_t NB, int max_chunk_len,
-                              int max_context_len) {
-  if (num_chunks < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1) return fail(PA_EINVAL, "bad sizes");
-  if (num_chunks > 0 && (!block_tables || !query_start_loc || !context_lens))
-    return fail(PA_EINVAL, "null pointer argument");
-  if (num_chunks > 0 && query_start_loc[0] != 0) return fail(PA_EINVAL, "query_start_loc[0] = %d, must be 0", query_start_loc[0]);
+// Chunk rules for sequences [first, first + n) of a batch whose chunk rows start at row0
+// (messages name the batch's own indices).
+static int check_chunks(const int32_t* block_tables, int max_blocks_per_seq,
+                        const int32_t* query_start_loc, const int32_t* context_lens, int first,
+                        int n, int32_t row0, int block_size, int64_t NB, int max_chunk_len,
+                        int max_context_len) {
+  if (n > 0 && query_start_loc[first] != row0)
+    return fail(PA_EINVAL, "query_start_loc[%d] = %d, must be %d", first, query_start_loc[first], row0);
   const long long cap = std::min<long long>(max_context_len, (long long)max_blocks_per_seq * block_size);
-  for (int c = 0; c < num_chunks; ++c) {
+  for (int c = first; c < first + n; ++c) {
     const int C = query_start_loc[c + 1] - query_start_loc[c];
     const int L = context_lens[c];
     if (C < 0) return fail(PA_EINVAL, "query_start_loc decreases at %d", c);
@@ -318,6 +431,36 @@ int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_se
     }
   }
   return ok();
+}
+
+int pa_validate_chunk_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int num_chunks, int block_size, int64_t NB, int max_chunk_len,
+                              int max_context_len) {
+  if (num_chunks < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1) return fail(PA_EINVAL, "bad sizes");
+  if (num_chunks > 0 && (!block_tables || !query_start_loc || !context_lens))
+    return fail(PA_EINVAL, "null pointer argument");
+  return check_chunks(block_tables, max_blocks_per_seq, query_start_loc, context_lens, 0,
+                      num_chunks, 0, block_size, NB, max_chunk_len, max_context_len);
+}
+
+int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_seq,
+                              const int32_t* query_start_loc, const int32_t* context_lens,
+                              int num_decodes, int num_chunks, int block_size, int64_t NB,
+                              int max_chunk_len, int max_context_len) {
+  if (num_decodes < 0 || num_chunks < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1)
+    return fail(PA_EINVAL, "bad sizes");
+  if (num_decodes + num_chunks > 0 && (!block_tables || !query_start_loc || !context_lens))
+    return fail(PA_EINVAL, "null pointer argument");
+  for (int b = 0; b <= num_decodes; ++b)
+    if (query_start_loc[b] != b)
+      return fail(PA_EINVAL, "query_start_loc[%d] = %d, a decode row must be %d", b, query_start_loc[b], b);
+  if (int r = pa_validate_decode_indices(block_tables, max_blocks_per_seq, context_lens,
+                                         num_decodes, block_size, NB, max_context_len))
+    return r;
+  return check_chunks(block_tables, max_blocks_per_seq, query_start_loc, context_lens,
+                      num_decodes, num_chunks, num_decodes, block_size, NB, max_chunk_len,
+                      max_context_len);
 }
 
 }  // extern "C"

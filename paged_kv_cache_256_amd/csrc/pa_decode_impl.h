@@ -1,0 +1,440 @@
+// pa_decode_impl.h -- the decode stream and merge bodies shared by the decode kernels and the
+// mixed-batch kernel (one wavefront's work each; the kernels only map hardware ids onto them).
+// The decomposition they implement is described at the top of pa_decode.hip.
+#pragma once
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace dec {
+
+constexpr int kWaves = 4;    // wavefronts per workgroup (each an independent worker)
+constexpr int kWgPerCu = 2;  // persistent workgroups per compute unit (2 waves per SIMD)
+constexpr int kIds = 64;     // block ids fetched per vector load
+
+// Cost units of a (sequence, kv head) run of nblk frames: one per frame plus kRestart for the
+// run's fixed start-up cost (about two memory latencies, i.e. roughly two frames of a
+// wavefront's streaming time).
+#ifndef PA_DECODE_RESTART_UNITS
+#define PA_DECODE_RESTART_UNITS 2
+#endif
+constexpr int kRestart = PA_DECODE_RESTART_UNITS;
+__host__ __device__ inline int run_units(int nblk) { return nblk > 0 ? nblk + kRestart : 0; }
+
+// Tile loads: non-temporal (not retained in the caches) when every frame is read once per call;
+// ordinary loads when frames are shared between sequences of the batch (copy-on-write branches,
+// cached prefixes), so that the sequences after the first find them in L2 / the MALL.
+template <bool NONTEMPORAL>
+__device__ inline u32x4 load_tile16(const u32x4* p) {
+  if constexpr (NONTEMPORAL) {
+    return __builtin_nontemporal_load(p);
+  } else {
+    return *p;
+  }
+}
+
+// Frames per pipeline step: two when a tile is 4 KiB or less (double-buffered K+V of two frames
+// = 128 VGPRs), one for larger tiles.
+template <int KIND, int D, int BS>
+constexpr int step_frames() { return KvOps<KIND, D, BS>::NL <= 4 ? 2 : 1; }
+
+template <int KIND>
+struct QType {
+  static constexpr int bytes = KIND == KF32 ? 4 : 2;
+};
+
+// The plan of a launch: plan[0] = U, the cost units of one kv head summed over the batch (the
+// launch holds F = Hkv * U units), then from plan[4] one int4 per wavefront w: the run (b, g)
+// holding unit a_w = floor(F w / W), the unit u of that run at which a_w falls, and the run's
+// unit count su.
+
+// Start of wavefront w found inside the wavefront itself (batches of at most kInlinePlanMax
+// sequences): lane l sums the units of sequences [l*per, (l+1)*per), a wave-wide scan gives every
+// lane its offset, a ballot finds the lane holding unit a_w / Hkv and a walk over its (at most 16)
+// sequences finds the run.
+constexpr int kInlinePlanMax = 1024;
+
+struct Start {
+  int b, g, u, su;
+  long long F;
+};
+
+__device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int B, int Hkv, int BS,
+                                  int cap, int W, int w, int lane) {
+  constexpr int kPer = kInlinePlanMax / 64;
+  const int per = (B + 63) / 64;
+  int un[kPer];
+  int mine = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int bb = lane * per + i;
+    const int L = (i < per && bb < B) ? max(0, min(context_lens[bb], cap)) : 0;
+    un[i] = run_units((L + BS - 1) / BS);
+    mine += un[i];
+  }
+  int incl = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  const int U = __builtin_amdgcn_readlane(incl, 63);
+  const int ex = incl - mine;
+  Start st;
+  st.F = (long long)Hkv * U;
+  const long long aw = st.F * w / W;
+  const int ap = (int)(aw / Hkv);
+  // lanes whose first offset is <= ap form a prefix; the last of them holds unit ap
+  const int k = __popcll(__ballot(ex <= ap)) - 1;
+  int cc = __builtin_amdgcn_readlane(ex, k);
+  int bb = k * per, su = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    if (i < per && bb < B) {
+      su = __builtin_amdgcn_readlane(un[i], k);
+      if (ap < cc + su) break;
+      cc += su;
+      ++bb;
+    }
+  }
+  const int off = (int)(aw - (long long)Hkv * cc);
+  st.b = bb;
+  st.g = su > 0 ? off / su : 0;
+  st.u = su > 0 ? off % su : 0;
+  st.su = su;
+  return st;
+}
+
+__device__ inline long long range_begin(long long F, int w, int W) { return F * w / W; }
+
+// The work of wavefront w out of the W wavefronts that split the batch.
+template <int KIND, int D, int BS, int F, bool NT>
+__device__ __forceinline__ void decode_stream_wave(
+    int w, int W, void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
+    const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
+    float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
+    long long NB, int cap, float qk_scale, float v_scale) {
+  using Ops = KvOps<KIND, D, BS>;
+  constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
+  constexpr int NGS = F * KG;  // 16-key groups per step
+  constexpr int QB = QType<KIND>::bytes;
+  constexpr size_t TILE = Ops::TILE;
+
+  const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
+
+  long long Ftot;
+  int b, g, u;  // u: unit within the run
+  if (inline_plan) {
+    const Start st = wave_plan(context_lens, B, Hkv, BS, cap, W, w, lane);
+    Ftot = st.F;
+    b = st.b;
+    g = st.g;
+    u = st.u;
+    if (lane == 0) {
+      ((int4*)(plan + 4))[w] = make_int4(st.b, st.g, st.u, st.su);
+      if (w == 0) plan[0] = (int)(Ftot / Hkv);
+    }
+  } else {
+    Ftot = (long long)Hkv * plan[0];
+    const int4 st = ((const int4*)(plan + 4))[w];
+    b = uniform(st.x);
+    g = uniform(st.y);
+    u = uniform(st.z);
+  }
+  const long long a = range_begin(Ftot, w, W), e = range_begin(Ftot, w + 1, W);
+  if (a >= e) return;
+
+  float m = -INFINITY, lsum = 0.f;
+  f32x4 acc[NC];
+  uint32_t qw[QW];
+
+  // frame ids of the current chunk (one per lane) and the lane stride of their loads: 1 for a
+  // live frame, 0 for a dead one (past the chunk, or an invalid id), which then reads the same
+  // 16 bytes of frame 0 in every lane -- the load stays unconditional but moves no tile
+  int vfid = 0, vstride = 0;
+  uint64_t live_mask = 0;
+  int L = 0, cblk = 0;  // context length and first block of the current chunk
+
+  auto load_step = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s) {
+    // keep a step's loads together and in order: the in-order load counter then lets the
+    // compute of the previous step wait for exactly its own data
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const int i = min(s * F + f, 63);
+      const int fr = __builtin_amdgcn_readlane(vfid, i);
+      const int ls = lane * __builtin_amdgcn_readlane(vstride, i);
+      const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
+      const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
+#pragma unroll
+      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16<NT>(kp + r * 64);
+#pragma unroll
+      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16<NT>(vp + r * 64);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Consume step s of the current chunk.  No loads in here: the only branch between a step's
+  // loads and this use is the loop back-edge, so the next step's loads stay in flight.
+  auto compute_step = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s) {
+    f32x4 sc[NGS];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+      const int i = s * F + f;
+      const bool live = i < 64 && ((live_mask >> i) & 1ull);
+      const int valid = live ? L - (cblk + i) * BS : 0;  // keys of this frame inside the context
+#pragma unroll
+      for (int h = 0; h < KG; ++h) {
+        f32x4 sv = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) sv = Ops::qk(sv, Ops::kop(kt[f], h, sl), Ops::qop(qw, sl));
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float v = (16 * h + 4 * j + ii < valid) ? sv[ii] * qk_scale : -INFINITY;
+          sc[f * KG + h][ii] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+      if (valid < BS) {
+        // dead frame, or the last frame of the context: clear V of the slots outside it so that
+        // whatever they hold (weighted by probability 0) cannot reach the accumulator
+#pragma unroll
+        for (int h = 0; h < KG; ++h) {
+          const int keep = min(4, max(0, valid - (16 * h + 4 * j)));
+#pragma unroll
+          for (int c = 0; c < NC; ++c) Ops::zero_quad(vt[f], h, c, keep);
+        }
+      }
+    }
+    mx = wave_max_over_j(mx);
+    const float mnew = fmaxf(m, mx);
+    if (mnew == -INFINITY) return;  // nothing live yet
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    m = mnew;
+    lsum *= alpha;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+    typename Ops::PFrag pf[NGS];
+#pragma unroll
+    for (int gi = 0; gi < NGS; ++gi) {
+      f32x4 p;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(sc[gi][ii] - mnew);
+      pf[gi] = Ops::pfrag(p, lsum);
+    }
+#pragma unroll
+    for (int pp = 0; pp < NGS / 2; ++pp) {
+      const int ga = 2 * pp, gb = 2 * pp + 1;
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        acc[c] = Ops::pv2(acc[c], Ops::vop(vt[ga / KG], ga % KG, c), Ops::vop(vt[gb / KG], gb % KG, c),
+                          pf[ga], pf[gb]);
+    }
+    if constexpr (NGS % 2) {
+      constexpr int gl = NGS - 1;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = Ops::pv(acc[c], Ops::vop(vt[gl / KG], gl % KG, c), pf[gl]);
+    }
+  };
+
+  u32x4 kA[F][NL], vA[F][NL], kB[F][NL], vB[F][NL];
+  long long x = a;
+  while (x < e && b < B) {
+    L = max(0, min(context_lens[b], cap));
+    const int nblk = (L + BS - 1) / BS;
+    const int units = (int)min((long long)(run_units(nblk) - u), e - x);  // of this run, here
+    // frames of the run inside this wavefront's range (its first kRestart units hold none)
+    const int f0 = max(0, u - kRestart), f1 = min(nblk, u + units - kRestart);
+    const int n_here = f1 - f0;
+    if (n_here > 0) {
+      const long long s0 = x - u;  // first unit of this (b, g) run
+      const bool complete = f0 == 0 && f1 == nblk;
+      const int blk = f0;
+      // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G)
+      {
+        const bool qv = n < G;
+        const size_t row = (size_t)b * Hq + (size_t)g * G + (qv ? n : 0);
+        const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
+#pragma unroll
+        for (int i = 0; i < QW / 4; ++i) {
+          u32x4 v4 = src[i];
+          if (!qv) v4 = (u32x4){0u, 0u, 0u, 0u};
+          qw[4 * i] = v4[0]; qw[4 * i + 1] = v4[1]; qw[4 * i + 2] = v4[2]; qw[4 * i + 3] = v4[3];
+        }
+      }
+      m = -INFINITY;
+      lsum = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+      for (int c0 = 0; c0 < n_here; c0 += kIds) {
+        const int cn = min(kIds, n_here - c0);
+        cblk = blk + c0;
+        const int f_raw = block_tables[(size_t)b * mbps + min(cblk + lane, nblk - 1)];
+        const bool ok = lane < cn && f_raw >= 0 && (long long)f_raw < NB;
+        live_mask = __ballot(ok);
+        vfid = ok ? f_raw : 0;
+        vstride = ok ? 1 : 0;
+        const int nsteps = (cn + F - 1) / F;
+        load_step(kA, vA, 0);
+        load_step(kB, vB, 1);
+        for (int s = 0; s < nsteps; s += 2) {
+          compute_step(kA, vA, s);
+          load_step(kA, vA, s + 2);
+          compute_step(kB, vB, s + 1);
+          load_step(kB, vB, s + 3);
+        }
+      }
+
+      const float lrow = wave_sum_over_j(lsum);
+      if (n < G) {
+        if (complete) {
+          const float inv = v_scale / lrow;
+          const size_t o = ((size_t)b * Hq + (size_t)g * G + n) * D + 4 * j;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            if constexpr (KIND == KF32) {
+              *(f32x4*)((float*)out + o + 16 * c) = acc[c] * inv;
+            } else {
+              u32x2 pk;
+              pk[0] = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
+              pk[1] = pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv);
+              *(u32x2*)((__bf16*)out + o + 16 * c) = pk;
+            }
+          }
+        } else {
+          const size_t row = ((size_t)w * 2 + (s0 > a ? 1 : 0)) * 16 + n;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) *(f32x4*)(ws_o + row * D + 16 * c + 4 * j) = acc[c];
+          if (j == 0) {
+            ws_ml[2 * row] = m;
+            ws_ml[2 * row + 1] = lrow;
+          }
+        }
+      }
+    }
+    x += units > 0 ? units : 0;
+    u = 0;
+    if (++g == Hkv) {
+      g = 0;
+      ++b;
+    }
+  }
+}
+
+// Merge the partials of the runs cut by wavefront range boundaries:
+// out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, M = max_w m_w (the final normalised
+// reduction of codebumble.net, "CUDA Shared Memory Optimization").  One wavefront per boundary k
+// (between the ranges of wavefronts k and k + 1) looks at the run holding unit a_{k+1}: if that
+// run has frames on both sides and k is the first boundary that cuts its frames, the wavefront
+// merges the partials of wavefronts w0..w1 (those holding the run's first and last frames; any
+// with an empty range hold none) in wavefront order.  Wavefront w keeps a run in partial slot 1
+// if the run began after the start of w's range (it is then w's last run), else in slot 0.
+// Lane (row rr = lane / 4, quarter qd = lane % 4) merges D/4 outputs of query row rr; the loads
+// of kBatch partials are in flight together.
+template <int KIND, int D>
+__device__ __forceinline__ void decode_reduce_wave(
+    int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
+    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
+  constexpr int kBatch = 4;
+  const int U = plan[0];
+  const int4 st = ((const int4*)(plan + 4))[k + 1];
+  const long long F = (long long)Hkv * U;
+  const long long a1 = F * (k + 1) / W;
+  const int u = st.z, su = st.w;
+  if (a1 >= F || u <= kRestart) return;  // no frames of this run before the boundary
+  const long long s0 = a1 - u;            // first unit of the run
+  const long long x0 = s0 + kRestart, x1 = s0 + su - 1;
+  // wavefront holding unit x: the largest w with floor(F w / W) <= x
+  const int w0 = (int)(((x0 + 1) * W + F - 1) / F - 1);
+  if (w0 != k) return;  // an earlier boundary cuts this run
+  const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
+  const int b = st.x, g = st.y;
+  // Gp = max(G, 4) rows of the group share the wavefront: lane -> (row rr, slice qd of
+  // D / lpr outputs), nv = D / (4 lpr) f32x4 per lane
+  const int Gp = G < 4 ? 4 : G;
+  const int lpr = 64 / Gp;
+  const int rr = lane / lpr, qd = lane % lpr;
+  const int nv = D / (4 * lpr);
+  constexpr int NV = D / 16;  // nv at most
+  float M = -INFINITY, den = 0.f;
+  f32x4 num[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) num[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // Wavefront w0 keeps the run in slot 1 if the run began after the start of its range; every
+  // later wavefront's range starts inside the run (slot 0).  When F >= W no range is empty and
+  // wavefronts w0..w1 all hold a partial; otherwise empty ones are skipped.
+  const long long aw0 = F * w0 / W;
+  const bool dense = F >= W;
+  for (int wb = w0; wb <= w1; wb += kBatch) {
+    f32x4 ob[kBatch][NV];
+    float mb[kBatch], lb[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int w = wb + i;
+      bool has = w <= w1;
+      if (!dense && has) has = F * w / W < F * (w + 1) / W;
+      const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
+      // rows past the group were never written: those lanes read nothing
+      const bool rd = has && rr < G;
+      const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
+      const f32x4* src = (const f32x4*)(ws_o + prow * D) + qd * nv;
+#pragma unroll
+      for (int v = 0; v < NV; ++v) ob[i][v] = (rd && v < nv) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      mb[i] = rd ? ws_ml[2 * prow] : -INFINITY;
+      lb[i] = rd ? ws_ml[2 * prow + 1] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (mb[i] == -INFINITY) continue;
+      if (mb[i] > M) {
+        const float sc = __builtin_amdgcn_exp2f(M - mb[i]);
+        den *= sc;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) num[v] *= sc;
+        M = mb[i];
+      }
+      const float ew = __builtin_amdgcn_exp2f(mb[i] - M);
+      den += ew * lb[i];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) num[v] += ew * ob[i][v];
+    }
+  }
+  if (rr >= G) return;
+  const float inv = v_scale / den;
+  const size_t o = ((size_t)b * Hq + (size_t)g * G + rr) * D + (size_t)qd * nv * 4;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    if (v >= nv) break;
+    if constexpr (KIND == KF32) {
+      *(f32x4*)((float*)out + o + 4 * v) = num[v] * inv;
+    } else {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(num[v][0] * inv, num[v][1] * inv);
+      pk[1] = pack_bf16x2(num[v][2] * inv, num[v][3] * inv);
+      *(u32x2*)((__bf16*)out + o + 4 * v) = pk;
+    }
+  }
+}
+
+// Workspace: the plan (4 ints, then an int4 per wavefront), then the two partial slots of every
+// wavefront (max and sum per row, then the 16 x D accumulator rows).
+struct Layout {
+  int W;
+  size_t plan_bytes, ml_bytes, o_bytes;
+};
+
+inline Layout layout(int D) {
+  Layout l;
+  l.W = device_compute_units() * kWgPerCu * kWaves;
+  l.plan_bytes = ((4 + 4 * (size_t)l.W) * sizeof(int32_t) + 255) / 256 * 256;
+  l.ml_bytes = (((size_t)l.W * 2 * 16 * 2) * sizeof(float) + 255) / 256 * 256;
+  l.o_bytes = (size_t)l.W * 2 * 16 * D * sizeof(float);
+  return l;
+}
+
+}  // namespace dec
+}  // namespace pa

@@ -47,7 +47,36 @@ struct PrefillParams {
   int kv_dtype;
   float k_scale, v_scale;
   void* workspace;
+  int64_t row_base;  // rows [0, row_base) of q / out belong to others; partials start there
 };
+
+// A mixed batch: sequences [0, num_decodes) are decodes (one query row each, row b), sequences
+// [num_decodes, num_decodes + num_chunks) are prefill chunks; block_tables, query_start_loc and
+// context_lens cover the whole batch.
+struct MixedParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int max_blocks_per_seq;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  int num_decodes, num_chunks;
+  int64_t total_q;
+  int max_chunk_len, max_context_len;
+  int64_t decode_tokens;  // sum of the decodes' context lengths (<= 0: unknown)
+  int Hq, Hkv, D, bs;
+  int64_t NB;
+  float scale;
+  int kv_dtype;
+  float k_scale, v_scale;
+  void* workspace;
+  bool shared_frames;
+  int mode;  // MixedMode
+};
+
+enum MixedMode { MIXED_AUTO = 0, MIXED_SPLIT = 1, MIXED_SEPARATE = 2 };
 
 // The calling thread's error message (pa_last_error): set_error formats it and returns `code`,
 // clear_error empties it and returns PA_OK.
@@ -60,10 +89,19 @@ int device_compute_units();
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+// The decode plan (wavefront starts) of W wavefronts, computed by one workgroup.
+hipError_t launch_decode_plan(const int32_t* context_lens, int32_t* plan, int B, int Hkv, int bs,
+                              int cap, int W, hipStream_t stream);
 
 size_t prefill_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
                                int max_context_len, int Hq, int Hkv, int D, int kv_dtype);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+size_t mixed_workspace_bytes(int num_decodes, int num_chunks, int64_t total_q, int max_chunk_len,
+                             int max_context_len, int Hq, int Hkv, int D, int kv_dtype);
+// Workgroups a mixed launch gives to prefill tiles (the rest run the decode stream).
+int mixed_prefill_workgroups(const MixedParams& p);
+hipError_t launch_mixed(const MixedParams& p, hipStream_t stream);
 
 hipError_t launch_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_cache,
                                     const int64_t* slots, int64_t T, int64_t NB, int Hkv, int D,

@@ -6,37 +6,27 @@
 // L - C + i and attends keys 0 .. L - C + i through the sequence's block table.
 //
 // The work is a dense contraction, so it runs on the matrix cores:
-//  * A workgroup (4 wavefronts) owns TQ chunk rows x the G heads of one kv head: each
-//    wavefront holds NT tiles of 16 query rows (row = token x head, so GQA heads of one token
-//    share every K/V fragment) as the columns of S^T = K Q^T.
-//  * K/V tiles are staged through LDS, 32 keys per stage, double-buffered: all 256 threads
-//    fetch the next stage's tiles with contiguous 16-byte loads while the wavefronts compute
-//    on the current one, and every wavefront then reads the same tile from LDS, so one fetch
-//    from L2/HBM serves 4 x NT x 16 query rows.
+//  * A workgroup (8 wavefronts, one workgroup per compute unit) owns TQ chunk rows x the G
+//    heads of one kv head: each wavefront holds NT tiles of 16 query rows (row = token x head,
+//    so GQA heads of one token share every K/V fragment) as the columns of S^T = K Q^T.
+//  * K/V tiles are staged through a ring of three LDS buffers, 32 keys per stage: all 512
+//    threads fetch a later stage with contiguous 16-byte loads while the wavefronts compute,
+//    and every wavefront then reads the same tile from LDS, so one fetch from L2/HBM serves
+//    8 x NT x 16 query rows.
 //  * Online softmax per query row (causal mask on the diagonal stages), O^T += V^T P^T with
-//    32-key 16x16x32 steps.
+//    32-key 16x16x32 steps; the score MFMAs of the next stage are issued inside the current
+//    stage's softmax.
 //  * The context is split into KS-key ranges across workgroups so that a single chunk fills
 //    the GPU; rows covered by one range are written directly, the others as unnormalised
 //    partials merged by prefill_reduce_kernel (log-sum-exp rule).
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "pa_prefill_impl.h"
 
 namespace pa {
 
+using namespace pre;
+
 namespace {
-
-constexpr int kPWaves = 8;      // wavefronts per workgroup (one workgroup per compute unit)
-constexpr int kTargetWGs = 256; // workgroups the context split aims for
-constexpr float kLazy = 8.f;    // log2-domain slack before the running shift moves
-
-// 16-row query tiles per wavefront (f32 operands take twice the registers).
-constexpr int tiles_per_wave(int kind) { return kind == KF32 ? 1 : 2; }
-
-template <int KIND>
-struct PQ {
-  static constexpr int bytes = KIND == KF32 ? 4 : 2;
-};
 
 template <int KIND, int D, int BS, int NT>
 __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
@@ -44,456 +34,35 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int mbps, int Hq, int Hkv, int G,
-    long long NB, long long total_q, int nsplit, int KS, int max_ctx, float qk_scale,
-    float v_scale) {
-  using Ops = KvOps<KIND, D, BS>;
-  constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
-  constexpr int TILE = Ops::TILE;
-  constexpr int SF = 32 / BS;            // frames per 32-key stage
-  constexpr int NG = SF * KG;            // 16-key groups per stage (= 2)
-  constexpr int STAGE = SF * 2 * TILE;   // bytes of K and V per stage
-  // bf16: K tiles [frame][tile] then V as the P.V operands: for head-dim block cc and lane l,
-  // 16 bytes = the 4 keys of 16-key group 0 then those of group 1 (one LDS read per MFMA).
-  // f32 / fp8: [frame][K, V][tile].
-  constexpr bool PAIRV = KIND == KBF16;
-  constexpr int NPIECE = STAGE / 16;                                 // 16-byte pieces per stage
-  constexpr int PPT = (NPIECE + kPWaves * 64 - 1) / (kPWaves * 64);  // pieces per thread
-  static_assert(NG == 2, "a stage is two 16-key groups");
-  static_assert(NPIECE % (kPWaves * 64) == 0 || PPT == 1, "stage must split over threads");
-  constexpr int QB = PQ<KIND>::bytes;
-
-  __shared__ __attribute__((aligned(16))) char smem[3][STAGE];
-
-  const int x = blockIdx.x, qt = blockIdx.y;
-  const int c = blockIdx.z / Hkv, g = blockIdx.z % Hkv;
-  const int w = uniform(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
-
-  const int r0 = qsl[c];
-  const int C = qsl[c + 1] - r0;
-  const int cap = min(max_ctx, mbps * BS);
-  const int L = min(context_lens[c], cap);
-  if (r0 < 0 || (long long)qsl[c + 1] > total_q || C <= 0 || C > L) return;
-  const int TQ = kPWaves * NT * 16 / G;
-  const int t0 = qt * TQ;
-  if (t0 >= C) return;
-  const int pos0 = L - C;
-  const int tq_end = min(t0 + TQ, C);
-  const int kbeg = x * KS;
-  const int kend = min(kbeg + KS, pos0 + tq_end);
-  if (kbeg >= kend) return;
-
-  // Query fragments and positions of this wavefront's NT tiles.  A negative score scale is
-  // moved into the query's sign bits (exact), so the scores scale by qk_abs >= 0 and a row's
-  // maximum can be taken on the unscaled products.
-  // (a zero scale is replaced by 1e-30: every product is then far below half an ulp of the
-  // row shift, so each probability is still exactly 1, and -inf * qk_abs stays -inf)
-  const float qk_abs = fmaxf(fabsf(qk_scale), 1e-30f);
-  const uint32_t qsign = qk_scale < 0.f ? (KIND == KF32 ? 0x80000000u : 0x80008000u) : 0u;
-  uint32_t qw[NT][QW];
-  int rpos[NT];
-  int rmin[NT];  // position of the tile's first row (the smallest), or -1 past the chunk
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int qrow = (w * NT + t) * 16 + n;
-    const int tok = t0 + qrow / G;
-    const bool ok = tok < C;
-    rpos[t] = ok ? pos0 + tok : -1;
-    {
-      const int tok0 = t0 + (w * NT + t) * 16 / G;
-      rmin[t] = tok0 < C ? pos0 + tok0 : -1;
-    }
-    const size_t row = (size_t)(r0 + (ok ? tok : 0)) * Hq + (size_t)g * G + qrow % G;
-    const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
-#pragma unroll
-    for (int i = 0; i < QW / 4; ++i) {
-      u32x4 v = src[i];
-      if (!ok) v = (u32x4){0u, 0u, 0u, 0u};
-      v ^= (u32x4){qsign, qsign, qsign, qsign};
-      qw[t][4 * i] = v[0]; qw[t][4 * i + 1] = v[1]; qw[t][4 * i + 2] = v[2]; qw[t][4 * i + 3] = v[3];
-    }
-  }
-
-  float m[NT], lsum[NT];
-  f32x4 acc[NT][NC];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    m[t] = -INFINITY;
-    lsum[t] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NC; ++cc) acc[t][cc] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int nst = (kend - kbeg + 31) / 32;
-  const size_t trow = (size_t)c * mbps;
-
-  // Fetch this thread's pieces of stage st into registers.  The loads are unconditional: a
-  // frame past kend, an invalid frame id or a stage past the last reads the same 16 bytes of
-  // frame 0 in every lane (its values are masked out or never used), so no branch separates
-  // a stage's loads from the wait that consumes them.
-  auto issue = [&](u32x4 (&buf)[PPT], int st) {
-    const int key0 = kbeg + 32 * st;
-    int fid[SF];
-#pragma unroll
-    for (int fl = 0; fl < SF; ++fl) {
-      const int fi = key0 / BS + fl;
-      int f = -1;
-      if (st < nst && fi * BS < kend) f = block_tables[trow + fi];
-      fid[fl] = uniform((f >= 0 && (long long)f < NB) ? f : -1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int p = threadIdx.x + k * kPWaves * 64;
-      const int fl = p / (2 * TILE / 16);
-      const int kind = (p / (TILE / 16)) & 1;
-      const int within = p % (TILE / 16);
-      int f = fid[0];
-#pragma unroll
-      for (int z = 1; z < SF; ++z)
-        if (fl == z) f = fid[z];
-      const char* base = kind ? v_cache : k_cache;
-      const u32x4* src = (f >= 0 && p < NPIECE)
-                             ? (const u32x4*)(base + ((size_t)f * Hkv + g) * TILE) + within
-                             : (const u32x4*)k_cache;
-      buf[k] = *src;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto stash = [&](const u32x4 (&buf)[PPT], int slot) {
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int p = threadIdx.x + k * kPWaves * 64;
-      if (!(NPIECE % (kPWaves * 64) == 0 || p < NPIECE)) continue;
-      if constexpr (PAIRV) {
-        const int fl = p / (2 * TILE / 16);
-        const int kind = (p / (TILE / 16)) & 1;
-        const int within = p % (TILE / 16);
-        if (kind == 0) {
-          *((u32x4*)(smem[slot] + fl * TILE) + within) = buf[k];
-        } else {
-          // piece r of the V tile holds quads u = 2r, 2r + 1 (u = key group h * NC + block c)
-          const int r = within >> 6, ll = within & 63;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int u = 2 * r + half;
-            const int gk = fl * KG + u / NC, cc = u % NC;
-            u32x2 v;
-            v[0] = buf[k][2 * half];
-            v[1] = buf[k][2 * half + 1];
-            *(u32x2*)(smem[slot] + SF * TILE + ((cc * 64 + ll) * 2 + gk) * 8) = v;
-          }
-        }
-      } else {
-        *((u32x4*)smem[slot] + p) = buf[k];
-      }
-    }
-  };
-
-  // Scores of stage st (K from LDS buffer st % 3).
-  auto qk = [&](int st, f32x4 (&s)[NT][NG]) {
-    const char* sb = smem[st % 3];
-#pragma unroll
-    for (int fl = 0; fl < SF; ++fl) {
-      u32x4 kt[NL];
-#pragma unroll
-      for (int r = 0; r < NL; ++r)
-        kt[r] = *((const u32x4*)(sb + (PAIRV ? fl : 2 * fl) * TILE + r * 1024) + lane);
-#pragma unroll
-      for (int h = 0; h < KG; ++h) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          f32x4 a = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int sl = 0; sl < NS; ++sl) a = Ops::qk(a, Ops::kop(kt, h, sl), Ops::qop(qw[t], sl));
-          s[t][fl * KG + h] = a;
-        }
-      }
-    }
-  };
-
-  // Softmax and P.V of stage st (V from LDS buffer st % 3).  `overlap` runs between the
-  // shift update and the exponentials, in the same basic block as the exponentials and the
-  // P.V products, so that the score MFMAs it issues for the next stage interleave with them.
-  auto finish = [&](int st, f32x4 (&s)[NT][NG], auto&& overlap) {
-    const char* sb = smem[st % 3];
-    const int key0 = kbeg + 32 * st;
-    // V operands of the stage (bf16: read before the softmax so that their latency hides
-    // behind it)
-    u32x4 vp[PAIRV ? NC : 1];
-    if constexpr (PAIRV) {
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) vp[cc] = *((const u32x4*)(sb + SF * TILE) + cc * 64 + lane);
-    }
-    // Online softmax per query row with a lazily moved shift: m[t] only moves (and the
-    // accumulators are rescaled) when a row's stage maximum exceeds it by more than kLazy in
-    // the log2 domain; otherwise the probabilities exp2(s - m) of the stage may exceed 1 (by at
-    // most 2^kLazy), which changes neither the normalised result nor the fp32 accumulation.
-    // One wavefront-uniform rescale decision per stage keeps the accumulators in place.  The
-    // causal / range mask is applied only on stages that reach past a row's position or the
-    // range end.
-    bool masked = key0 + 32 > kend;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) masked = masked || key0 + 31 > rmin[t];
-    if (masked) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-          for (int ii = 0; ii < 4; ++ii) {
-            const int key = key0 + 16 * gi + 4 * j + ii;
-            s[t][gi][ii] = (key < kend && key <= rpos[t]) ? s[t][gi][ii] : -INFINITY;
-          }
-      if constexpr (PAIRV) {
-        // keys past the range end may be unwritten slots: clear their values
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
-          const uint32_t m0 = keep >= 2 ? 0xffffffffu : (keep == 1 ? 0x0000ffffu : 0u);
-          const uint32_t m1 = keep >= 4 ? 0xffffffffu : (keep == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            vp[cc][2 * gi] &= m0;
-            vp[cc][2 * gi + 1] &= m1;
-          }
-        }
-      }
-    }
-    float mxs[NT];
-    bool grow = false;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[t][gi][ii]);
-      mx = wave_max_over_j(mx);
-      mx = mx == -INFINITY ? -INFINITY : mx * qk_abs;  // scores scale by qk_abs >= 0
-      mxs[t] = mx;
-      grow = grow || mx > m[t] + kLazy;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float mnew = fmaxf(m[t], mxs[t]);
-        const float alpha = m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[t] - mnew);
-        m[t] = mnew;
-        lsum[t] *= alpha;
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
-      }
-    }
-    overlap();
-    typename Ops::PFrag pf[NT][NG];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float nm = m[t] == -INFINITY ? 0.f : -m[t];
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        f32x4 p;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          // a masked score is -inf and qk_abs > 0: its probability is exactly 0
-          p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][gi][ii], qk_abs, nm));
-        }
-        pf[t][gi] = Ops::pfrag(p, lsum[t]);
-      }
-    }
-    // P * V
-    if constexpr (PAIRV) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        u32x4 pb;
-        pb[0] = pf[t][0][0]; pb[1] = pf[t][0][1]; pb[2] = pf[t][1][0]; pb[3] = pf[t][1][1];
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) acc[t][cc] = mfma_x32_bf16(vp[cc], pb, acc[t][cc]);
-      }
-    } else {
-      u32x4 vt[SF][NL];
-#pragma unroll
-      for (int fl = 0; fl < SF; ++fl)
-#pragma unroll
-        for (int r = 0; r < NL; ++r) vt[fl][r] = *((const u32x4*)(sb + (2 * fl + 1) * TILE + r * 1024) + lane);
-      if (key0 + 32 > kend) {
-        // keys past the range end may be unwritten slots: clear their values
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[gi / KG], gi % KG, cc, keep);
-        }
-      }
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const auto va = Ops::vop(vt[0], 0, cc);
-        const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
-      }
-    }
-  };
-
-  // Software pipeline over a ring of three LDS stages: while the softmax and P.V of stage st
-  // run on the vector ALUs, the score MFMAs of stage st + 1 are already issued, and stage
-  // st + 2 moves from registers into LDS; stage st + 3 is in flight from memory.
-  u32x4 pre[PPT];
-  issue(pre, 0);
-  stash(pre, 0);
-  issue(pre, 1);
-  stash(pre, 1);
-  issue(pre, 2);
-  __syncthreads();
-  f32x4 sa[NT][NG], sz[NT][NG];
-  qk(0, sa);
-  for (int st = 0; st < nst; st += 2) {
-    // (past the last stage the next-stage scores read a ring buffer already written and are
-    // never used: issuing them unconditionally keeps them in the exponentials' block)
-    finish(st, sa, [&] { qk(st + 1, sz); });
-    if (st + 2 < nst) stash(pre, (st + 2) % 3);
-    issue(pre, st + 3);
-    __syncthreads();
-    if (st + 1 >= nst) break;
-    finish(st + 1, sz, [&] { qk(st + 2, sa); });
-    if (st + 3 < nst) stash(pre, (st + 3) % 3);
-    issue(pre, st + 4);
-    __syncthreads();
-  }
-
-  // Results: direct output for rows covered by a single key range, partials otherwise.
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float lrow = wave_sum_over_j(lsum[t]);
-    if (rpos[t] < kbeg) continue;  // no key of this range is visible to the row
-    const int qrow = (w * NT + t) * 16 + n;
-    const size_t r = (size_t)r0 + (rpos[t] - pos0);
-    const size_t h = (size_t)g * G + qrow % G;
-    const int nsp = min(nsplit, rpos[t] / KS + 1);
-    if (nsp == 1) {
-      const float inv = v_scale / lrow;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const size_t o = (r * Hq + h) * D + 16 * cc + 4 * j;
-        if constexpr (KIND == KF32) {
-          *(f32x4*)((float*)out + o) = acc[t][cc] * inv;
-        } else {
-          u32x2 pk;
-          pk[0] = pack_bf16x2(acc[t][cc][0] * inv, acc[t][cc][1] * inv);
-          pk[1] = pack_bf16x2(acc[t][cc][2] * inv, acc[t][cc][3] * inv);
-          *(u32x2*)((__bf16*)out + o) = pk;
-        }
-      }
-    } else {
-      const size_t pi = (r * Hq + h) * nsplit + x;
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) *(f32x4*)(ws_o + pi * D + 16 * cc + 4 * j) = acc[t][cc];
-      if (j == 0) {
-        ws_ml[2 * pi] = m[t];
-        ws_ml[2 * pi + 1] = lrow;
-      }
-    }
-  }
+    long long NB, long long total_q, long long row_base, int nsplit, int KS, int max_ctx,
+    float qk_scale, float v_scale) {
+  __shared__ __attribute__((aligned(16))) char smem[3][prefill_stage_bytes<KIND, D, BS>()];
+  prefill_tile<KIND, D, BS, NT>(&smem[0][0], blockIdx.x, blockIdx.y, blockIdx.z / Hkv, blockIdx.z % Hkv,
+                                row_base, out, q, k_cache, v_cache, block_tables, qsl, context_lens,
+                                ws_ml, ws_o, mbps, Hq, Hkv, G, NB, total_q, nsplit, KS, max_ctx,
+                                qk_scale, v_scale);
 }
 
-// Merge the context splits of every (row, head) whose keys span more than one split:
-// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.  One wavefront per
-// (row, head), four per workgroup; lane l merges head-dim elements [l*NV, (l+1)*NV).  All of a
-// row's partials are loaded before any is used.
 template <int KIND, int D>
 __global__ __launch_bounds__(256) void prefill_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int num_chunks,
-    long long total_q, int Hq, int nsplit, int KS, int cap, float v_scale) {
-  constexpr int NV = D / 64;       // outputs per lane
-  constexpr int kMaxSplit = 16;    // partials held in registers at once
-  const long long pair = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (pair >= total_q * Hq) return;
-  const long long r = pair / Hq;
-  const int h = (int)(pair - r * Hq);
-  int lo = 0, hi = num_chunks - 1;  // last chunk c with qsl[c] <= r
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) / 2;
-    if (qsl[mid] <= r) lo = mid; else hi = mid - 1;
-  }
-  const int c = lo;
-  const int C = qsl[c + 1] - qsl[c];
-  const int L = min(context_lens[c], cap);
-  if (r < qsl[c] || r >= qsl[c + 1] || C <= 0 || C > L) return;
-  const int pos = L - C + (int)(r - qsl[c]);
-  const int nsp = min(nsplit, pos / KS + 1);
-  if (nsp <= 1) return;
-  const size_t base = ((size_t)r * Hq + h) * nsplit;
-  float M = -INFINITY, den = 0.f, num[NV];
-#pragma unroll
-  for (int v = 0; v < NV; ++v) num[v] = 0.f;
-  for (int p0 = 0; p0 < nsp; p0 += kMaxSplit) {
-    float mp[kMaxSplit], lp[kMaxSplit], op[kMaxSplit][NV];
-#pragma unroll
-    for (int i = 0; i < kMaxSplit; ++i) {
-      const bool has = p0 + i < nsp;
-      const size_t q = base + (has ? p0 + i : 0);
-      mp[i] = has ? ws_ml[2 * q] : -INFINITY;
-      lp[i] = has ? ws_ml[2 * q + 1] : 0.f;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) op[i][v] = has ? ws_o[q * D + lane * NV + v] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kMaxSplit; ++i) {
-      if (mp[i] == -INFINITY) continue;
-      if (mp[i] > M) {
-        const float sc = __builtin_amdgcn_exp2f(M - mp[i]);
-        den *= sc;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) num[v] *= sc;
-        M = mp[i];
-      }
-      const float e = __builtin_amdgcn_exp2f(mp[i] - M);
-      den += e * lp[i];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) num[v] += e * op[i][v];
-    }
-  }
-  const size_t o = ((size_t)r * Hq + h) * D + lane * NV;
-#pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const float x = num[v] / den * v_scale;
-    if constexpr (KIND == KF32) {
-      ((float*)out)[o + v] = x;
-    } else {
-      ((__bf16*)out)[o + v] = (__bf16)x;
-    }
-  }
-}
-
-struct Split {
-  int nsplit, KS;
-};
-
-Split choose_split(int num_chunks, int max_chunk_len, int max_ctx, int Hq, int Hkv, int kind) {
-  const int G = Hq / Hkv;
-  const int TQ = kPWaves * tiles_per_wave(kind) * 16 / G;
-  const long long tiles = (long long)num_chunks * ((max_chunk_len + TQ - 1) / TQ) * Hkv;
-  int want = (int)((kTargetWGs + tiles - 1) / (tiles > 0 ? tiles : 1));
-  const int most = (max_ctx + 255) / 256;
-  if (want > most) want = most;
-  if (want < 1) want = 1;
-  int KS = (max_ctx + want - 1) / want;
-  KS = ((KS + 63) / 64) * 64;
-  if (KS < 64) KS = 64;
-  return Split{(max_ctx + KS - 1) / KS, KS};
+    long long total_q, long long row_base, int Hq, int nsplit, int KS, int cap, float v_scale) {
+  prefill_reduce_wave<KIND, D>((long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63,
+                               row_base, out, ws_ml, ws_o, qsl, context_lens, num_chunks, total_q, Hq,
+                               nsplit, KS, cap, v_scale);
 }
 
 template <int KIND, int D, int BS>
 hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   constexpr int NT = tiles_per_wave(KIND);
-  const Split sp = choose_split(p.num_chunks, p.max_chunk_len, p.max_context_len, p.Hq, p.Hkv, KIND);
+  const Split sp = choose_split(p.num_chunks, p.max_chunk_len, p.max_context_len, p.Hq, p.Hkv, KIND,
+                                device_compute_units());
   const int G = p.Hq / p.Hkv;
   const int TQ = kPWaves * NT * 16 / G;
   float* ws_ml = (float*)p.workspace;
-  float* ws_o = ws_ml ? ws_ml + (size_t)2 * p.total_q * p.Hq * sp.nsplit : nullptr;
+  const long long rows = p.total_q - p.row_base;  // rows of the chunks
+  float* ws_o = ws_ml ? ws_ml + (size_t)2 * rows * p.Hq * sp.nsplit : nullptr;
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
   dim3 grid(sp.nsplit, (p.max_chunk_len + TQ - 1) / TQ, p.num_chunks * p.Hkv);
@@ -501,15 +70,17 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
                      stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
                      p.block_tables, p.query_start_loc, p.context_lens, ws_ml, ws_o,
                      p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB,
-                     (long long)p.total_q, sp.nsplit, sp.KS, p.max_context_len, qk_scale, v_scale);
+                     (long long)p.total_q, (long long)p.row_base, sp.nsplit, sp.KS,
+                     p.max_context_len, qk_scale, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.nsplit <= 1) return e;
   const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
                                                                  : p.max_blocks_per_seq * BS;
-  const long long pairs = p.total_q * p.Hq;
+  const long long pairs = rows * p.Hq;
   hipLaunchKernelGGL((prefill_reduce_kernel<KIND, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
                      stream, p.out, ws_ml, ws_o, p.query_start_loc, p.context_lens, p.num_chunks,
-                     (long long)p.total_q, p.Hq, sp.nsplit, sp.KS, cap, v_scale);
+                     (long long)p.total_q, (long long)p.row_base, p.Hq, sp.nsplit, sp.KS, cap,
+                     v_scale);
   return hipGetLastError();
 }
 
@@ -529,7 +100,8 @@ hipError_t launch_prefill_kind(const PrefillParams& p, hipStream_t s) {
 size_t prefill_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
                                int max_context_len, int Hq, int Hkv, int D, int kv_dtype) {
   const int kind = kv_dtype == DT_F32 ? KF32 : (kv_dtype == DT_BF16 ? KBF16 : KFP8);
-  const Split sp = choose_split(num_chunks, max_chunk_len, max_context_len, Hq, Hkv, kind);
+  const Split sp = choose_split(num_chunks, max_chunk_len, max_context_len, Hq, Hkv, kind,
+                                device_compute_units());
   if (sp.nsplit <= 1) return 0;
   return (size_t)total_q * Hq * sp.nsplit * (2 + (size_t)D) * sizeof(float);
 }

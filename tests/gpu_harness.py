@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import paged_kv_cache_256_amd as pa
+import workloads
 
 
 def device():
@@ -93,6 +94,27 @@ class GpuStep:
                              k_scale=c.k_scale, v_scale=c.v_scale,
                              shared_frames=kw.pop("shared_frames", c.shares_frames), **kw)
         return self.out
+
+    def mixed(self, decode_tokens=None, **kw):
+        """pa_mixed_attention over the case's decodes and chunks as one batch (decodes first);
+        returns the output split into (decode rows, chunk rows)."""
+        c, dev = self.c, self.dev
+        m = workloads.mixed_batch(c)
+        if not hasattr(self, "_mixed_in"):
+            self._mixed_in = (to_dev(m.q, c.q_dtype, dev), to_dev(m.block_tables, "i32", dev),
+                              to_dev(m.query_start_loc, "i32", dev),
+                              to_dev(m.context_lens, "i32", dev))
+        q, tables, qsl, lens = self._mixed_in
+        out = pa.mixed_attention(q, self.kc, self.vc, tables, qsl, lens, m.num_decodes,
+                                 block_size=c.bs, scale=c.scale, kv_dtype=c.kv_dtype,
+                                 max_chunk_len=max(m.max_chunk_len, 1),
+                                 max_context_len=m.max_context_len,
+                                 decode_tokens=m.decode_tokens if decode_tokens is None else decode_tokens,
+                                 k_scale=c.k_scale, v_scale=c.v_scale,
+                                 shared_frames=kw.pop("shared_frames", c.shares_frames),
+                                 mode=kw.pop("mode", "auto"), **kw)
+        self.mixed_out = out
+        return out[:c.B], out[c.B:]
 
     def step(self):
         self.write()

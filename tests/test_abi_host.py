@@ -259,3 +259,100 @@ def test_decode_ex_rejects_unknown_flags():
     assert f(*args, 1 << 31, NULL) == EINVAL
     # flag 1 (shared frames) is accepted: the call then fails only on the fake workspace size
     assert f(*(args[:-1] + [0]), 1, NULL) == ENOSPC
+
+
+# ----------------------------------------------------------------------------- pa_mixed_attention
+
+
+def mixed(**kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, mbps=8, qsl=FAKE, cl=FAKE, nd=4, nc=2,
+             tq=44, mcl=32, mctx=128, dtok=300, Hq=8, Hkv=2, D=64, bs=16, NB=64, scale=0.1,
+             qd=BF16, kvd=BF16, ks=1.0, vs=1.0, ws=NULL, wsb=0, flags=0)
+    a.update(kw)
+    return lib().pa_mixed_attention(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["mbps"],
+                                    a["qsl"], a["cl"], a["nd"], a["nc"], a["tq"], a["mcl"],
+                                    a["mctx"], a["dtok"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                    a["NB"], a["scale"], a["qd"], a["kvd"], a["ks"], a["vs"],
+                                    a["ws"], a["wsb"], a["flags"], NULL)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(qsl=NULL), EINVAL, "null pointer"),
+    (dict(cl=NULL), EINVAL, "null pointer"),
+    (dict(nd=-1), EINVAL, "bad sizes"),
+    (dict(tq=3), EINVAL, "bad sizes"),
+    (dict(nd=70000, tq=80000), ENOTSUP, "decodes too many"),
+    (dict(mcl=200, mctx=100), EINVAL, "max_chunk_len"),
+    (dict(mctx=0), EINVAL, "max_context_len"),
+    (dict(nc=40000, Hkv=2), ENOTSUP, "num_chunks * Hkv"),
+    (dict(tq=1 << 31), ENOTSUP, "total_q"),
+    (dict(D=256), ENOTSUP, "head_dim"),
+    (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
+    (dict(qd=F32, kvd=FP8), ENOTSUP, "dtype combination"),
+    (dict(kvd=FP8, ks=-1.0), EINVAL, "fp8 scales"),
+    (dict(scale=float("nan")), EINVAL, "scale"),
+    (dict(flags=8), EINVAL, "unknown flags"),
+    (dict(flags=2 | 4), EINVAL, "exclude each other"),
+])
+def test_mixed_rejects_bad_arguments(kw, code, msg):
+    assert mixed(**kw) == code
+    assert msg in err()
+
+
+def test_mixed_workspace_and_empty_batch():
+    f = lib().pa_mixed_workspace_bytes
+    need = f(4, 2, 44, 32, 128, 8, 2, 64, 16, BF16)
+    # the decode half alone needs what pa_decode needs
+    assert need >= lib().pa_decode_workspace_bytes(4, 8, 64, 16, BF16, 128) > 0
+    assert f(0, 2, 40, 32, 128, 8, 2, 64, 16, BF16) == lib().pa_prefill_chunk_workspace_bytes(
+        2, 40, 32, 128, 8, 2, 64, 16, BF16)
+    assert f(4, 0, 4, 0, 128, 8, 2, 64, 16, BF16) >= lib().pa_decode_workspace_bytes(
+        4, 8, 64, 16, BF16, 128)
+    assert f(4, 2, 3, 32, 128, 8, 2, 64, 16, BF16) == 0  # fewer rows than decodes
+    assert mixed(ws=NULL, wsb=0) == ENOSPC
+    assert mixed(ws=FAKE, wsb=need - 1) == ENOSPC
+    assert mixed(nd=0, nc=0, tq=0, out=NULL) == OK
+    # flags 1 (shared frames), 2 (split) and 4 (separate) are accepted
+    for fl in (1, 2, 4, 1 | 2, 1 | 4):
+        assert mixed(ws=FAKE, wsb=need - 1, flags=fl) == ENOSPC
+
+
+def test_mixed_mode_choice_follows_the_sizes():
+    f = lib().pa_mixed_prefill_units
+    cus = f(0, 1, 512, 512, 16384, 0, 32, 8, 128, 16, BF16, 0)  # chunks only: every CU
+    assert cus > 0
+    assert f(128, 0, 128, 0, 16384, 0, 32, 8, 128, 16, BF16, 0) == 0  # decodes only
+    assert f(128, 1, 640, 512, 16384, 128 * 2176, 32, 8, 128, 16, BF16, 4) == cus
+    split = f(128, 1, 640, 512, 16384, 128 * 2176, 32, 8, 128, 16, BF16, 2)
+    assert 0 < split < cus
+    # a huge decode share never takes the split, whatever the chunk
+    assert f(128, 1, 640, 512, 16384, 10 ** 12, 32, 8, 128, 16, BF16, 0) == cus
+    # more decode bytes never give the prefill half more compute units
+    last = cus
+    for dtok in (10 ** 4, 10 ** 5, 3 * 10 ** 5, 10 ** 6, 3 * 10 ** 6):
+        p = f(128, 1, 640, 512, 16384, dtok, 32, 8, 128, 16, BF16, 2)
+        assert 0 < p <= last
+        last = p
+    assert f(128, 1, 640, 512, 16384, 0, 32, 8, 128, 16, BF16, 6) == -1
+    assert f(-1, 1, 640, 512, 16384, 0, 32, 8, 128, 16, BF16, 0) == -1
+
+
+def test_validate_mixed_indices():
+    bt = np.array([[0, 1, 2], [3, 4, 5], [6, 7, 8]], np.int32)
+    qsl = np.array([0, 1, 11, 31], np.int32)  # one decode, then chunks of 10 and 20 rows
+    cl = np.array([33, 40, 20], np.int32)
+    pa.validate_mixed_indices(bt, qsl, cl, 1, 16, 9, 20, 48)
+    with pytest.raises(pa.PAError, match="a decode row must be"):
+        pa.validate_mixed_indices(bt, np.array([0, 2, 11, 31], np.int32), cl, 1, 16, 9, 20, 48)
+    with pytest.raises(pa.PAError, match="rows but context length"):
+        pa.validate_mixed_indices(bt, qsl, np.array([33, 40, 19], np.int32), 1, 16, 9, 20, 48)
+    with pytest.raises(pa.PAError, match=r"context_lens\[0\]"):
+        pa.validate_mixed_indices(bt, qsl, np.array([49, 40, 20], np.int32), 1, 16, 9, 20, 48)
+    with pytest.raises(pa.PAError, match=r"block_tables\[2\]\[0\]"):
+        pa.validate_mixed_indices(bt, qsl, cl, 1, 16, 6, 20, 48)  # frame 6 outside NB = 6
+    with pytest.raises(pa.PAError, match=r"chunk 2 has 20 rows > max_chunk_len 19"):
+        pa.validate_mixed_indices(bt, qsl, cl, 1, 16, 9, 19, 48)
+    pa.validate_mixed_indices(bt, np.array([0, 1, 2, 3], np.int32), np.array([5, 6, 7], np.int32),
+                              3, 16, 9, 1, 48)  # decodes only
+    with pytest.raises(ValueError):
+        pa.validate_mixed_indices(bt, qsl[:-1], cl, 1, 16, 9, 20, 48)

@@ -492,3 +492,34 @@ def test_two_chunks_of_n_equal_one_chunk_of_2n():
     two = oracle.prefill_chunk(q, kc, vc, np.concatenate([table, table]), np.array([0, n, 2 * n]),
                                np.array([L - n, L]), **kw)
     np.testing.assert_array_equal(two, whole)
+
+
+def test_mixed_step_equals_decodes_and_chunks_alone():
+    import workloads
+
+    c = workloads.chunk_case("mix", 17, Hq=8, Hkv=2, D=64, bs=16,
+                             chunks=[(20, 70), (16, 16), (5, 40)], decode_lens=[1, 5, 33, 48],
+                             kv_dtype="bf16", std=0.7071)
+    kw = dict(bs=c.bs, src_dtype=c.src_dtype, kv_dtype=c.kv_dtype, k_scale=c.k_scale,
+              v_scale=c.v_scale)
+    kc = oracle.new_cache(c.NB, c.Hkv, c.bs, c.D, c.kv_dtype)
+    vc = oracle.new_cache(c.NB, c.Hkv, c.bs, c.D, c.kv_dtype)
+    oracle.reshape_and_cache(kc, vc, c.pool_k, c.pool_v, c.pool_slots, **kw)
+    oracle.reshape_and_cache(kc, vc, c.new_k, c.new_v, c.new_slots, **kw)
+    m = workloads.mixed_batch(c)
+    akw = dict(scale=c.scale, bs=c.bs, q_dtype=c.q_dtype, kv_dtype=c.kv_dtype,
+               k_scale=c.k_scale, v_scale=c.v_scale)
+    mixed = oracle.mixed_attention(m.q, kc, vc, m.block_tables, m.query_start_loc,
+                                   m.context_lens, m.num_decodes, **akw)
+    dec = oracle.decode(c.q, kc, vc, c.block_tables, c.context_lens, **akw)
+    ch = c.chunk
+    chunk = oracle.prefill_chunk(ch.q, kc, vc, ch.block_tables, ch.query_start_loc,
+                                 ch.context_lens, **akw)
+    assert mixed.shape[0] == c.B + ch.q.shape[0]
+    np.testing.assert_array_equal(mixed[:c.B], dec)
+    np.testing.assert_array_equal(mixed[c.B:], chunk)
+    bad = m.query_start_loc.copy()
+    bad[1] = 2
+    with pytest.raises(ValueError):
+        oracle.mixed_attention(m.q, kc, vc, m.block_tables, bad, m.context_lens, m.num_decodes,
+                               **akw)

@@ -15,6 +15,8 @@ from .cases import (  # noqa: F401
     decode_case,
     chunk_case,
     fork_case,
+    mixed_batch,
+    MixedBatch,
     CONFIG_NAMES,
     POISON_K,
     POISON_V,

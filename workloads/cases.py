@@ -295,6 +295,44 @@ def chunk_case(name: str, seed: int, *, Hq: int, Hkv: int, D: int, bs: int, chun
                       chunk=chunk, meta={"live_slots": int(live.sum())})
 
 
+@dataclass
+class MixedBatch:
+    """A case's decodes and prefill chunks as one batch, decodes first: query row b is decode b,
+    the chunks' rows follow; query_start_loc, context_lens and block_tables cover every
+    sequence of the batch."""
+
+    q: np.ndarray  # [B + chunk rows, Hq, D]
+    query_start_loc: np.ndarray  # int32 [B + num_chunks + 1]
+    context_lens: np.ndarray  # int32 [B + num_chunks]
+    block_tables: np.ndarray  # int32 [B + num_chunks, width]
+    num_decodes: int
+    decode_tokens: int  # sum of the decodes' context lengths
+    max_chunk_len: int
+    max_context_len: int
+
+
+def mixed_batch(case: DecodeCase) -> MixedBatch:
+    """Concatenate the decodes and the chunks of `case` (bookkeeping only)."""
+    B, ch = case.B, case.chunk
+    nc = ch.num_chunks if ch is not None else 0
+    parts = [case.block_tables[:B]] + ([ch.block_tables] if nc else [])
+    width = max(max(p.shape[1] for p in parts), 1)
+    tables = np.full((B + nc, width), -1, dtype=np.int32)
+    tables[:B, :case.block_tables.shape[1]] = case.block_tables[:B]
+    if nc:
+        tables[B:, :ch.block_tables.shape[1]] = ch.block_tables
+    q = np.concatenate([case.q[:B]] + ([ch.q] if nc else []), axis=0)
+    qsl = np.arange(B + 1, dtype=np.int32)
+    if nc:
+        qsl = np.concatenate([qsl[:B], B + ch.query_start_loc.astype(np.int32)])
+    lens = np.concatenate([case.context_lens[:B]] + ([ch.context_lens] if nc else [])).astype(np.int32)
+    return MixedBatch(q=q, query_start_loc=qsl.astype(np.int32), context_lens=lens,
+                      block_tables=tables, num_decodes=B,
+                      decode_tokens=int(case.context_lens[:B].astype(np.int64).sum()),
+                      max_chunk_len=ch.max_chunk_len if nc else 0,
+                      max_context_len=int(lens.max()) if len(lens) else 1)
+
+
 def fork_case(name: str, seed: int, *, prompts: int = 32, branches: int = 8,
               prompt_len: int = 1024, tail_lo: int = 64, tail_hi: int = 512, Hq: int = 64,
               Hkv: int = 8, D: int = 128, bs: int = 32, kv_dtype: str = "fp8",
