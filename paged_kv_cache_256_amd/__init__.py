@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     BlockManager,
     LIB_PATH,
     PAError,
+    PreparedCall,
     build_info,
     copy_blocks,
     decode,

@@ -101,6 +101,38 @@ def _check(status: int):
         raise PAError(status, last_error())
 
 
+class PreparedCall:
+    """A library call whose arguments were checked and marshalled once (raw device pointers, the
+    stream current at preparation).  Calling it issues the same call again; the tensors it was
+    prepared from must stay alive and keep their storage."""
+
+    __slots__ = ("_fn", "_args")
+
+    def __init__(self, fn, args):
+        self._fn = fn
+        self._args = tuple(a if isinstance(a, ctypes._SimpleCData) else t(a)
+                           for a, t in zip(args, fn.argtypes))
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            raise PAError(status, last_error())
+
+
+def _issue(fn, args, prepared: bool):
+    if prepared:
+        return PreparedCall(fn, args)
+    _check(fn(*args))
+    return None
+
+
+def _need_outputs(prepared: bool, **bufs):
+    if prepared:
+        missing = [k for k, v in bufs.items() if v is None]
+        if missing:
+            raise ValueError(f"a prepared call needs its {', '.join(missing)} passed in")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -134,7 +166,7 @@ def new_kv_cache(NB: int, Hkv: int, block_size: int, D: int, kv_dtype: str, devi
 
 
 def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, block_size: int, kv_dtype: str,
-                      k_scale: float = 1.0, v_scale: float = 1.0):
+                      k_scale: float = 1.0, v_scale: float = 1.0, prepared: bool = False):
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     src = {torch.float32: "f32", torch.bfloat16: "bf16"}.get(k.dtype)
     if src is None or v.dtype != k.dtype:
@@ -146,17 +178,19 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, block_size: int, 
             _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
             _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, Hkv, D, block_size,
             DTYPE_CODE[src], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), _stream(k))
-    _check(_lib.pa_reshape_and_cache(*args))
+    return _issue(_lib.pa_reshape_and_cache, args, prepared)
 
 
-def copy_blocks(k_cache, v_cache, pairs, *, block_size: int, kv_dtype: str):
+def copy_blocks(k_cache, v_cache, pairs, *, block_size: int, kv_dtype: str,
+                prepared: bool = False):
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     if pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be [N, 2]")
-    _check(_lib.pa_copy_blocks(_dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
-                               _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
-                               _dev(pairs, "pairs", torch.int64), pairs.shape[0], NB, Hkv, D,
-                               block_size, DTYPE_CODE[kv_dtype], _stream(k_cache)))
+    return _issue(_lib.pa_copy_blocks,
+                  (_dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+                   _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+                   _dev(pairs, "pairs", torch.int64), pairs.shape[0], NB, Hkv, D, block_size,
+                   DTYPE_CODE[kv_dtype], _stream(k_cache)), prepared)
 
 
 def decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len) -> int:
@@ -170,9 +204,11 @@ def q_dtype_for(kv_dtype: str) -> str:
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, scale: float,
            kv_dtype: str, max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0,
-           out=None, workspace=None, shared_frames: bool = False):
+           out=None, workspace=None, shared_frames: bool = False, prepared: bool = False):
     """pa_decode_ex; shared_frames=True when frames appear in several sequences' tables (keeps
-    them cacheable; the result is bit-identical either way)."""
+    them cacheable; the result is bit-identical either way).  prepared=True returns a
+    PreparedCall (out and workspace must be given) instead of running the call."""
+    _need_outputs(prepared, out=out, workspace=workspace)
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     qd = q_dtype_for(kv_dtype)
     B, Hq, Dq = q.shape
@@ -188,15 +224,16 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, 
     if os.environ.get("PA_VALIDATE") == "1":
         validate_decode_indices(block_tables.cpu().numpy(), context_lens.cpu().numpy(),
                                 block_size, NB, max_context_len)
-    _check(_lib.pa_decode_ex(_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
-                             _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
-                             _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
-                             _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
-                             _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D,
-                             block_size, NB, float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype],
-                             float(k_scale), float(v_scale), int(max_context_len), ws, wsb,
-                             PA_DECODE_SHARED_FRAMES if shared_frames else 0, _stream(q)))
-    return out
+    args = (_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+            _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, block_size, NB,
+            float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale),
+            int(max_context_len), ws, wsb, PA_DECODE_SHARED_FRAMES if shared_frames else 0,
+            _stream(q))
+    call = _issue(_lib.pa_decode_ex, args, prepared)
+    return call if prepared else out
 
 
 def prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,
@@ -209,7 +246,8 @@ def prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_contex
 def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_lens, *,
                   block_size: int, scale: float, kv_dtype: str, max_chunk_len: int,
                   max_context_len: int, k_scale: float = 1.0, v_scale: float = 1.0, out=None,
-                  workspace=None):
+                  workspace=None, prepared: bool = False):
+    _need_outputs(prepared, out=out)
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     qd = q_dtype_for(kv_dtype)
     total_q, Hq, Dq = q.shape
@@ -220,6 +258,8 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_le
         out = torch.empty_like(q)
     need = prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq,
                                          Hkv, D, block_size, kv_dtype)
+    if need:
+        _need_outputs(prepared, workspace=workspace)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
@@ -228,15 +268,15 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_le
         validate_chunk_indices(block_tables.cpu().numpy(), query_start_loc.cpu().numpy(),
                                context_lens.cpu().numpy(), block_size, NB, max_chunk_len,
                                max_context_len)
-    _check(_lib.pa_prefill_chunk(
+    call = _issue(_lib.pa_prefill_chunk, (
         _dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
         _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]), _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
         _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
         _dev(query_start_loc, "query_start_loc", torch.int32, 1),
         _dev(context_lens, "context_lens", torch.int32, 1), num_chunks, total_q, int(max_chunk_len),
         int(max_context_len), Hq, Hkv, D, block_size, NB, float(scale), DTYPE_CODE[qd],
-        DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), ws, wsb, _stream(q)))
-    return out
+        DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), ws, wsb, _stream(q)), prepared)
+    return call if prepared else out
 
 
 def mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len, Hq,
@@ -267,12 +307,13 @@ def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_
                     num_decodes: int, *, block_size: int, scale: float, kv_dtype: str,
                     max_chunk_len: int, max_context_len: int, decode_tokens: int = 0,
                     k_scale: float = 1.0, v_scale: float = 1.0, out=None, workspace=None,
-                    shared_frames: bool = False, mode: str = "auto"):
+                    shared_frames: bool = False, mode: str = "auto", prepared: bool = False):
     """pa_mixed_attention: the first num_decodes sequences are decodes (query row b), the rest
     prefill chunks; one kernel runs both.  decode_tokens (sum of the decodes' context lengths,
     known on the host) and mode ("auto", "split": one kernel runs both halves side by side,
     "separate": the chunk kernels then the decode kernels) only decide how the call uses the
     device."""
+    _need_outputs(prepared, out=out)
     NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
     qd = q_dtype_for(kv_dtype)
     total_q, Hq, Dq = q.shape
@@ -286,6 +327,8 @@ def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_
         out = torch.empty_like(q)
     need = mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len,
                                  Hq, Hkv, D, block_size, kv_dtype)
+    if need:
+        _need_outputs(prepared, workspace=workspace)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
@@ -294,7 +337,7 @@ def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_
         validate_mixed_indices(block_tables.cpu().numpy(), query_start_loc.cpu().numpy(),
                                context_lens.cpu().numpy(), num_decodes, block_size, NB,
                                max_chunk_len, max_context_len)
-    _check(_lib.pa_mixed_attention(
+    call = _issue(_lib.pa_mixed_attention, (
         _dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
         _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]), _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
         _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
@@ -302,8 +345,8 @@ def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_
         _dev(context_lens, "context_lens", torch.int32, 1), int(num_decodes), num_chunks, total_q,
         int(max_chunk_len), int(max_context_len), int(decode_tokens), Hq, Hkv, D, block_size, NB,
         float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale), ws,
-        wsb, _mixed_flags(shared_frames, mode), _stream(q)))
-    return out
+        wsb, _mixed_flags(shared_frames, mode), _stream(q)), prepared)
+    return call if prepared else out
 
 
 # ----------------------------------------------------------------------------- host validators

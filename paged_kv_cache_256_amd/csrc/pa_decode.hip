@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 template <int KIND, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   constexpr int F = step_frames<KIND, D, BS>();
-  const Layout l = layout(D);
+  const Layout l = layout(D, stream_waves());
   int32_t* plan = (int32_t*)p.workspace;
   float* ws_ml = (float*)((char*)p.workspace + l.plan_bytes);
   float* ws_o = (float*)((char*)p.workspace + l.plan_bytes + l.ml_bytes);
@@ -172,7 +172,7 @@ hipError_t launch_kind(const DecodeParams& p, hipStream_t s) {
 
 size_t decode_workspace_bytes(int /*B*/, int /*Hq*/, int D, int /*bs*/, int /*kv_dtype*/,
                               int /*max_context_len*/) {
-  const Layout l = layout(D);
+  const Layout l = layout(D, stream_waves());
   return l.plan_bytes + l.ml_bytes + l.o_bytes;
 }
 

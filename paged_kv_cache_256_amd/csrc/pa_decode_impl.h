@@ -10,8 +10,20 @@ namespace pa {
 namespace dec {
 
 constexpr int kWaves = 4;    // wavefronts per workgroup (each an independent worker)
-constexpr int kWgPerCu = 2;  // persistent workgroups per compute unit (2 waves per SIMD)
+constexpr int kWgPerCu = 2;  // register budget: two workgroups per CU (256 VGPRs a wavefront)
 constexpr int kIds = 64;     // block ids fetched per vector load
+
+// Wavefronts of a decode launch per compute unit.  Measured on MI355X over the 8B / 70B shapes,
+// bf16 and fp8: 3 per CU (192 four-wavefront workgroups on 256 CUs, 24 per XCD) streams 4-6%
+// faster than 8 per CU; with 8 per CU some 64 MB of tile loads are in flight, far past what HBM
+// needs to stay busy, and the excess only queues.  Launches whose workgroups do not spread evenly
+// over the CUs (5 or 6 per CU) are 10-15% slower.
+constexpr int kStreamWavesPerCu = 3;
+
+inline int stream_waves() {
+  const int w = device_compute_units() * kStreamWavesPerCu / kWaves * kWaves;
+  return w > kWaves ? w : kWaves;
+}
 
 // Cost units of a (sequence, kv head) run of nblk frames: one per frame plus kRestart for the
 // run's fixed start-up cost (about two memory latencies, i.e. roughly two frames of a
@@ -427,9 +439,10 @@ struct Layout {
   size_t plan_bytes, ml_bytes, o_bytes;
 };
 
-inline Layout layout(int D) {
+// Workspace of a launch of up to W wavefronts.
+inline Layout layout(int D, int W) {
   Layout l;
-  l.W = device_compute_units() * kWgPerCu * kWaves;
+  l.W = W;
   l.plan_bytes = ((4 + 4 * (size_t)l.W) * sizeof(int32_t) + 255) / 256 * 256;
   l.ml_bytes = (((size_t)l.W * 2 * 16 * 2) * sizeof(float) + 255) / 256 * 256;
   l.o_bytes = (size_t)l.W * 2 * 16 * D * sizeof(float);

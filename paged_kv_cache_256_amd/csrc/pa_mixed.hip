@@ -205,7 +205,7 @@ MixedLayout mixed_layout(int num_decodes, int num_chunks, long long crows, int m
                          int max_context_len, int Hq, int Hkv, int D, int kv_dtype) {
   MixedLayout l{0, 0, 1};
   if (num_decodes > 0) {
-    const Layout d = layout(D);
+    const Layout d = layout(D, device_compute_units() * kPWaves);
     l.dec_bytes = d.plan_bytes + d.ml_bytes + (d.o_bytes + 255) / 256 * 256;
   }
   if (num_chunks > 0 && crows > 0) {
@@ -249,7 +249,7 @@ hipError_t launch_mixed_typed(const MixedParams& p, hipStream_t stream) {
   const bool has_d = p.num_decodes > 0;
   const int grid = cus;
   const int Wd = (grid - roles.P) * kPWaves;
-  const Layout dl = layout(D);
+  const Layout dl = layout(D, cus * kPWaves);
   char* ws = (char*)p.workspace;
 
   MixedArgs a{};

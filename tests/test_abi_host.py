@@ -356,3 +356,12 @@ def test_validate_mixed_indices():
                               3, 16, 9, 1, 48)  # decodes only
     with pytest.raises(ValueError):
         pa.validate_mixed_indices(bt, qsl[:-1], cl, 1, 16, 9, 20, 48)
+
+
+def test_prepared_calls_need_their_buffers_passed_in():
+    with pytest.raises(ValueError, match="out, workspace"):
+        pa.decode(None, None, None, None, None, block_size=16, scale=0.1, kv_dtype="bf16",
+                  max_context_len=16, prepared=True)
+    with pytest.raises(ValueError, match="out"):
+        pa.prefill_chunk(None, None, None, None, None, None, block_size=16, scale=0.1,
+                         kv_dtype="bf16", max_chunk_len=16, max_context_len=16, prepared=True)

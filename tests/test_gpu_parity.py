@@ -368,3 +368,40 @@ def test_shared_frames_hint_gives_identical_bits(shared):
     assert c.shares_frames == (shared == "fork")
     o = OracleStep(c)
     assert np.abs(out_f64(b) - o.decode()).max() <= tolerance(c)
+
+
+def test_prepared_calls_match_ordinary_calls_bit_for_bit():
+    c = workloads.chunk_case("prepared", 77, Hq=16, Hkv=4, D=128, bs=16, chunks=[(96, 700)],
+                             decode_lens=[5, 300, 1200, 2048], kv_dtype="fp8", std=0.7071)
+    g = GpuStep(c)
+    g.write()
+    d0 = g.decode().clone()
+    c0 = g.prefill().clone()
+    _, m0 = g.mixed(mode="split")
+    m0 = m0.clone()
+    ws = torch.empty(pa.decode_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype,
+                                               c.max_context_len), dtype=torch.uint8,
+                     device=g.dev)
+    out = torch.zeros_like(g.q)
+    call = pa.decode(g.q, g.kc, g.vc, g.tables, g.lens, block_size=c.bs, scale=c.scale,
+                     kv_dtype=c.kv_dtype, max_context_len=c.max_context_len, k_scale=c.k_scale,
+                     v_scale=c.v_scale, out=out, workspace=ws, prepared=True)
+    assert isinstance(call, pa.PreparedCall) and not out.any()
+    ch = c.chunk
+    cws = torch.empty(max(1, pa.prefill_chunk_workspace_bytes(
+        ch.num_chunks, g.cq.shape[0], ch.max_chunk_len, ch.max_context_len, c.Hq, c.Hkv, c.D,
+        c.bs, c.kv_dtype)), dtype=torch.uint8, device=g.dev)
+    cout = torch.zeros_like(g.cq)
+    pcall = pa.prefill_chunk(g.cq, g.kc, g.vc, g.ctables, g.cqsl, g.clens, block_size=c.bs,
+                             scale=c.scale, kv_dtype=c.kv_dtype, max_chunk_len=ch.max_chunk_len,
+                             max_context_len=ch.max_context_len, k_scale=c.k_scale,
+                             v_scale=c.v_scale, out=cout, workspace=cws, prepared=True)
+    for _ in range(2):
+        call()
+        pcall()
+        torch.cuda.synchronize()
+        assert torch.equal(out, d0)
+        assert torch.equal(cout, c0)
+    _, m1 = g.mixed(mode="split")
+    torch.cuda.synchronize()
+    assert torch.equal(m1, m0)
