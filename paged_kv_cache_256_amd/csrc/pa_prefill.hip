@@ -9,13 +9,14 @@
 //  * A workgroup (8 wavefronts, one workgroup per compute unit) owns TQ chunk rows x the G
 //    heads of one kv head: each wavefront holds NT tiles of 16 query rows (row = token x head,
 //    so GQA heads of one token share every K/V fragment) as the columns of S^T = K Q^T.
-//  * K/V tiles are staged through a ring of three LDS buffers, 32 keys per stage: all 512
-//    threads fetch a later stage with contiguous 16-byte loads while the wavefronts compute,
-//    and every wavefront then reads the same tile from LDS, so one fetch from L2/HBM serves
-//    8 x NT x 16 query rows.
+//  * K/V tiles are staged through a ring of four LDS buffers, 64 keys per stage (32 for f32):
+//    each wavefront copies its share of a later stage straight from global memory into LDS with
+//    LDS-DMA loads while the wavefronts compute, and every wavefront then reads the same tile
+//    from LDS, so one fetch from L2/HBM serves 8 x NT x 16 query rows.  One meeting point per
+//    stage; the copies of the next two stages stay in flight across it.
 //  * Online softmax per query row (causal mask on the diagonal stages), O^T += V^T P^T with
-//    32-key 16x16x32 steps; the score MFMAs of the next stage are issued inside the current
-//    stage's softmax.
+//    16x16x32 products over pairs of 16-key groups; the score MFMAs of the next stage are issued
+//    inside the current stage's softmax.
 //  * The context is split into KS-key ranges across workgroups so that a single chunk fills
 //    the GPU; rows covered by one range are written directly, the others as unnormalised
 //    partials merged by prefill_reduce_kernel (log-sum-exp rule).
@@ -36,8 +37,9 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int mbps, int Hq, int Hkv, int G,
     long long NB, long long total_q, long long row_base, int nsplit, int KS, int max_ctx,
     float qk_scale, float v_scale) {
-  __shared__ __attribute__((aligned(16))) char smem[3][prefill_stage_bytes<KIND, D, BS>()];
-  prefill_tile<KIND, D, BS, NT>(&smem[0][0], blockIdx.x, blockIdx.y, blockIdx.z / Hkv, blockIdx.z % Hkv,
+  constexpr int S = prefill_stage_bytes<KIND, D, BS>();
+  __shared__ __attribute__((aligned(1024))) char ring0[S], ring1[S], ring2[S], ring3[S];
+  prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, blockIdx.x, blockIdx.y, blockIdx.z / Hkv, blockIdx.z % Hkv,
                                 row_base, out, q, k_cache, v_cache, block_tables, qsl, context_lens,
                                 ws_ml, ws_o, mbps, Hq, Hkv, G, NB, total_q, nsplit, KS, max_ctx,
                                 qk_scale, v_scale);

@@ -20,17 +20,32 @@ struct PQ {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// Bytes of K and V per 32-key stage in LDS.
+// One LDS-DMA copy (global_load_lds_dwordx4): each lane's 16 bytes at src land at lds + 16 lane.
+// Issued as assembly so that the compiler does not make unrelated LDS reads wait for it (the
+// pipeline below waits for the copies itself); the kernels that use it leave M0 to it.
+__device__ inline void lds_dma16(const void* src, char* lds) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
+               : "memory");
+}
+
+// Keys per pipeline stage: 64 (32 for f32, whose tiles are twice as large: a ring of four 64-key
+// stages would not fit LDS).  64-key stages halve the per-stage costs (the meeting point, the
+// rescale decision, the masks) against 32-key ones: 3-10% faster on bf16 / fp8 chunks.
+constexpr int stage_keys(int kind) { return kind == KF32 ? 32 : 64; }
+
+// Bytes of K and V per stage in LDS.
 template <int KIND, int D, int BS>
 constexpr int prefill_stage_bytes() {
-  return (32 / BS) * 2 * KvOps<KIND, D, BS>::TILE;
+  return (stage_keys(KIND) / BS) * 2 * KvOps<KIND, D, BS>::TILE;
 }
 
 // One workgroup's tile: context range x (keys [x KS, (x+1) KS)), query tile qt of chunk c, kv
 // head g.  Rows are absolute rows of q / out; partials are indexed from row_base.
 template <int KIND, int D, int BS, int NT>
 __device__ __forceinline__ void prefill_tile(
-    char* smem_base, int x, int qt, int c, int g,
+    char* ring0, char* ring1, char* ring2, char* ring3, int x, int qt, int c, int g,
     long long row_base, void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
@@ -40,21 +55,14 @@ __device__ __forceinline__ void prefill_tile(
   using Ops = KvOps<KIND, D, BS>;
   constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
   constexpr int TILE = Ops::TILE;
-  constexpr int SF = 32 / BS;            // frames per 32-key stage
-  constexpr int NG = SF * KG;            // 16-key groups per stage (= 2)
+  constexpr int SK = stage_keys(KIND);   // keys per stage
+  constexpr int SF = SK / BS;            // frames per stage
+  constexpr int NG = SF * KG;            // 16-key groups per stage
   constexpr int STAGE = SF * 2 * TILE;   // bytes of K and V per stage
-  // bf16: K tiles [frame][tile] then V as the P.V operands: for head-dim block cc and lane l,
-  // 16 bytes = the 4 keys of 16-key group 0 then those of group 1 (one LDS read per MFMA).
-  // f32 / fp8: [frame][K, V][tile].
-  constexpr bool PAIRV = KIND == KBF16;
-  constexpr int NPIECE = STAGE / 16;                                 // 16-byte pieces per stage
-  constexpr int PPT = (NPIECE + kPWaves * 64 - 1) / (kPWaves * 64);  // pieces per thread
-  static_assert(NG == 2, "a stage is two 16-key groups");
-  static_assert(NPIECE % (kPWaves * 64) == 0 || PPT == 1, "stage must split over threads");
+  static_assert(NG % 2 == 0, "a stage is pairs of 16-key groups");
   constexpr int QB = PQ<KIND>::bytes;
 
   static_assert(STAGE == prefill_stage_bytes<KIND, D, BS>(), "stage size");
-  char (*smem)[STAGE] = reinterpret_cast<char (*)[STAGE]>(smem_base);  // the 3-stage LDS ring
 
   const int w = uniform(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
@@ -114,15 +122,22 @@ __device__ __forceinline__ void prefill_tile(
     for (int cc = 0; cc < NC; ++cc) acc[t][cc] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
 
-  const int nst = (kend - kbeg + 31) / 32;
+  const int nst = (kend - kbeg + SK - 1) / SK;
   const size_t trow = (size_t)c * mbps;
 
-  // Fetch this thread's pieces of stage st into registers.  The loads are unconditional: a
-  // frame past kend, an invalid frame id or a stage past the last reads the same 16 bytes of
-  // frame 0 in every lane (its values are masked out or never used), so no branch separates
-  // a stage's loads from the wait that consumes them.
-  auto issue = [&](u32x4 (&buf)[PPT], int st) {
-    const int key0 = kbeg + 32 * st;
+  // Staging of a stage: its K and V tiles are NBLK blocks of 1 KiB in the cache's tile
+  // layout (a block holds one 16-byte fragment per lane), stored in LDS as [frame][K, V][block].
+  // Wavefront w copies blocks w, w + 8, ... straight from global memory into the stage's LDS
+  // buffer with LDS-DMA loads (lane l's 16 bytes land at the block's base + 16 l): no register or
+  // LDS store of the wavefront carries them, and the copy of a later stage runs while this one
+  // is computed.  Frames past kend, invalid ids and stages past the last copy the first 16 bytes
+  // of the K cache instead (never used), so every stage issues the same loads and the wait
+  // counts below hold.
+  constexpr int NBLK = STAGE / 1024;
+  constexpr int BPW = (NBLK + kPWaves - 1) / kPWaves;  // blocks per wavefront and stage
+  static_assert(NBLK % kPWaves == 0 || NBLK < kPWaves, "stage blocks must split over waves");
+  auto dma = [&](char* buf, int st) {
+    const int key0 = kbeg + SK * st;
     int fid[SF];
 #pragma unroll
     for (int fl = 0; fl < SF; ++fl) {
@@ -131,64 +146,40 @@ __device__ __forceinline__ void prefill_tile(
       if (st < nst && fi * BS < kend) f = block_tables[trow + fi];
       fid[fl] = uniform((f >= 0 && (long long)f < NB) ? f : -1);
     }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int p = threadIdx.x + k * kPWaves * 64;
-      const int fl = p / (2 * TILE / 16);
-      const int kind = (p / (TILE / 16)) & 1;
-      const int within = p % (TILE / 16);
+    for (int k = 0; k < BPW; ++k) {
+      const int blk = w + k * kPWaves;
+      if (NBLK < kPWaves && blk >= NBLK) break;  // wavefront-uniform
+      const int fl = blk / (2 * NL), kind = (blk / NL) & 1, r = blk % NL;
       int f = fid[0];
 #pragma unroll
       for (int z = 1; z < SF; ++z)
         if (fl == z) f = fid[z];
       const char* base = kind ? v_cache : k_cache;
-      const u32x4* src = (f >= 0 && p < NPIECE)
-                             ? (const u32x4*)(base + ((size_t)f * Hkv + g) * TILE) + within
-                             : (const u32x4*)k_cache;
-      buf[k] = *src;
+      const u32x4* src = f >= 0 ? (const u32x4*)(base + ((size_t)f * Hkv + g) * TILE + r * 1024) + lane
+                                : (const u32x4*)k_cache;
+      lds_dma16(src, buf + blk * 1024);
     }
-    __builtin_amdgcn_sched_barrier(0);
   };
-  auto stash = [&](const u32x4 (&buf)[PPT], int slot) {
-#pragma unroll
-    for (int k = 0; k < PPT; ++k) {
-      const int p = threadIdx.x + k * kPWaves * 64;
-      if (!(NPIECE % (kPWaves * 64) == 0 || p < NPIECE)) continue;
-      if constexpr (PAIRV) {
-        const int fl = p / (2 * TILE / 16);
-        const int kind = (p / (TILE / 16)) & 1;
-        const int within = p % (TILE / 16);
-        if (kind == 0) {
-          *((u32x4*)(smem[slot] + fl * TILE) + within) = buf[k];
-        } else {
-          // piece r of the V tile holds quads u = 2r, 2r + 1 (u = key group h * NC + block c)
-          const int r = within >> 6, ll = within & 63;
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int u = 2 * r + half;
-            const int gk = fl * KG + u / NC, cc = u % NC;
-            u32x2 v;
-            v[0] = buf[k][2 * half];
-            v[1] = buf[k][2 * half + 1];
-            *(u32x2*)(smem[slot] + SF * TILE + ((cc * 64 + ll) * 2 + gk) * 8) = v;
-          }
-        }
-      } else {
-        *((u32x4*)smem[slot] + p) = buf[k];
-      }
+  // Wait until this wavefront's copies of every stage but the newest have landed in LDS, then
+  // meet the other wavefronts (after which their copies have landed too).  Written as assembly:
+  // the compiler's barrier would also wait for the newest stage's copies.
+  auto sync_stage = [&]() {
+    if (NBLK >= kPWaves || w < NBLK) {
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(BPW) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
   };
 
   // Scores of stage st (K from LDS buffer st % 3).
-  auto qk = [&](int st, f32x4 (&s)[NT][NG]) {
-    const char* sb = smem[st % 3];
+  auto qk = [&](const char* sb, f32x4 (&s)[NT][NG]) {
 #pragma unroll
     for (int fl = 0; fl < SF; ++fl) {
       u32x4 kt[NL];
 #pragma unroll
       for (int r = 0; r < NL; ++r)
-        kt[r] = *((const u32x4*)(sb + (PAIRV ? fl : 2 * fl) * TILE + r * 1024) + lane);
+        kt[r] = *((const u32x4*)(sb + 2 * fl * TILE + r * 1024) + lane);
 #pragma unroll
       for (int h = 0; h < KG; ++h) {
 #pragma unroll
@@ -205,16 +196,8 @@ __device__ __forceinline__ void prefill_tile(
   // Softmax and P.V of stage st (V from LDS buffer st % 3).  `overlap` runs between the
   // shift update and the exponentials, in the same basic block as the exponentials and the
   // P.V products, so that the score MFMAs it issues for the next stage interleave with them.
-  auto finish = [&](int st, f32x4 (&s)[NT][NG], auto&& overlap) {
-    const char* sb = smem[st % 3];
-    const int key0 = kbeg + 32 * st;
-    // V operands of the stage (bf16: read before the softmax so that their latency hides
-    // behind it)
-    u32x4 vp[PAIRV ? NC : 1];
-    if constexpr (PAIRV) {
-#pragma unroll
-      for (int cc = 0; cc < NC; ++cc) vp[cc] = *((const u32x4*)(sb + SF * TILE) + cc * 64 + lane);
-    }
+  auto finish = [&](int st, const char* sb, f32x4 (&s)[NT][NG], auto&& overlap) {
+    const int key0 = kbeg + SK * st;
     // Online softmax per query row with a lazily moved shift: m[t] only moves (and the
     // accumulators are rescaled) when a row's stage maximum exceeds it by more than kLazy in
     // the log2 domain; otherwise the probabilities exp2(s - m) of the stage may exceed 1 (by at
@@ -222,9 +205,9 @@ __device__ __forceinline__ void prefill_tile(
     // One wavefront-uniform rescale decision per stage keeps the accumulators in place.  The
     // causal / range mask is applied only on stages that reach past a row's position or the
     // range end.
-    bool masked = key0 + 32 > kend;
+    bool masked = key0 + SK > kend;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) masked = masked || key0 + 31 > rmin[t];
+    for (int t = 0; t < NT; ++t) masked = masked || key0 + SK - 1 > rmin[t];
     if (masked) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
@@ -235,20 +218,6 @@ __device__ __forceinline__ void prefill_tile(
             const int key = key0 + 16 * gi + 4 * j + ii;
             s[t][gi][ii] = (key < kend && key <= rpos[t]) ? s[t][gi][ii] : -INFINITY;
           }
-      if constexpr (PAIRV) {
-        // keys past the range end may be unwritten slots: clear their values
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-          const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
-          const uint32_t m0 = keep >= 2 ? 0xffffffffu : (keep == 1 ? 0x0000ffffu : 0u);
-          const uint32_t m1 = keep >= 4 ? 0xffffffffu : (keep == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            vp[cc][2 * gi] &= m0;
-            vp[cc][2 * gi + 1] &= m1;
-          }
-        }
-      }
     }
     float mxs[NT];
     bool grow = false;
@@ -291,28 +260,26 @@ __device__ __forceinline__ void prefill_tile(
         pf[t][gi] = Ops::pfrag(p, lsum[t]);
       }
     }
-    // P * V
-    if constexpr (PAIRV) {
+    // P * V over pairs of 16-key groups (one 16x16x32 product each); with 16-key frames the two
+    // groups are two frames, with 32-key frames the two halves of one
+    const bool tail = key0 + SK > kend;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        u32x4 pb;
-        pb[0] = pf[t][0][0]; pb[1] = pf[t][0][1]; pb[2] = pf[t][1][0]; pb[3] = pf[t][1][1];
+    for (int pp = 0; pp < NG / 2; ++pp) {
+      constexpr int FPP = KG == 1 ? 2 : 1;  // frames per pair
+      u32x4 vt[FPP][NL];
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) acc[t][cc] = mfma_x32_bf16(vp[cc], pb, acc[t][cc]);
-      }
-    } else {
-      u32x4 vt[SF][NL];
+      for (int fl = 0; fl < FPP; ++fl)
 #pragma unroll
-      for (int fl = 0; fl < SF; ++fl)
-#pragma unroll
-        for (int r = 0; r < NL; ++r) vt[fl][r] = *((const u32x4*)(sb + (2 * fl + 1) * TILE + r * 1024) + lane);
-      if (key0 + 32 > kend) {
+        for (int r = 0; r < NL; ++r)
+          vt[fl][r] = *((const u32x4*)(sb + (2 * (pp * FPP + fl) + 1) * TILE + r * 1024) + lane);
+      if (tail) {
         // keys past the range end may be unwritten slots: clear their values
 #pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
+        for (int h = 0; h < 2; ++h) {
+          const int gi = 2 * pp + h;
           const int keep = min(4, max(0, kend - (key0 + 16 * gi + 4 * j)));
 #pragma unroll
-          for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[gi / KG], gi % KG, cc, keep);
+          for (int cc = 0; cc < NC; ++cc) Ops::zero_quad(vt[h / KG], h % KG, cc, keep);
         }
       }
 #pragma unroll
@@ -321,36 +288,43 @@ __device__ __forceinline__ void prefill_tile(
         const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
+          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][2 * pp], pf[t][2 * pp + 1]);
       }
     }
   };
 
-  // Software pipeline over a ring of three LDS stages: while the softmax and P.V of stage st
-  // run on the vector ALUs, the score MFMAs of stage st + 1 are already issued, and stage
-  // st + 2 moves from registers into LDS; stage st + 3 is in flight from memory.
-  u32x4 pre[PPT];
-  issue(pre, 0);
-  stash(pre, 0);
-  issue(pre, 1);
-  stash(pre, 1);
-  issue(pre, 2);
-  __syncthreads();
+  // Software pipeline over a ring of four LDS stage buffers: while the softmax and P.V of stage
+  // st run on the vector ALUs, the score MFMAs of stage st + 1 are already issued and the copies
+  // of stages st + 2 and st + 3 are in flight.  Stage st + 3 goes into the buffer of stage st - 1,
+  // which every wavefront finished reading before the previous meeting point.
+  dma(ring0, 0);
+  dma(ring1, 1);
+  dma(ring2, 2);
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   f32x4 sa[NT][NG], sz[NT][NG];
-  qk(0, sa);
-  for (int st = 0; st < nst; st += 2) {
-    // (past the last stage the next-stage scores read a ring buffer already written and are
-    // never used: issuing them unconditionally keeps them in the exponentials' block)
-    finish(st, sa, [&] { qk(st + 1, sz); });
-    if (st + 2 < nst) stash(pre, (st + 2) % 3);
-    issue(pre, st + 3);
-    __syncthreads();
+  qk(ring0, sa);
+  // one stage: copy stage st + 3 into the buffer stage st - 1 used, finish stage st (its scores
+  // in s_cur) while the scores of stage st + 1 go into s_nxt, meet
+  auto stage = [&](int st, const char* cur, const char* nxt, char* free_buf, f32x4 (&s_cur)[NT][NG],
+                   f32x4 (&s_nxt)[NT][NG]) {
+    dma(free_buf, st + 3);
+    // (past the last stage the next-stage scores read a buffer already written and are never
+    // used: issuing them unconditionally keeps them in the exponentials' block)
+    finish(st, cur, s_cur, [&] { qk(nxt, s_nxt); });
+    sync_stage();
+  };
+  for (int st = 0; st < nst; st += 4) {
+    stage(st, ring0, ring1, ring3, sa, sz);
     if (st + 1 >= nst) break;
-    finish(st + 1, sz, [&] { qk(st + 2, sa); });
-    if (st + 3 < nst) stash(pre, (st + 3) % 3);
-    issue(pre, st + 4);
-    __syncthreads();
+    stage(st + 1, ring1, ring2, ring0, sz, sa);
+    if (st + 2 >= nst) break;
+    stage(st + 2, ring2, ring3, ring1, sa, sz);
+    if (st + 3 >= nst) break;
+    stage(st + 3, ring3, ring0, ring2, sz, sa);
   }
+  // copies of stages past the last are still in flight: let them land before the buffers are
+  // reused or the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // Results: direct output for rows covered by a single key range, partials otherwise.
 #pragma unroll
