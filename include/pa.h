@@ -135,8 +135,9 @@ size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype 
  *                 written this step (write it with pa_reshape_and_cache first, on the
  *                 same stream).
  *   max_context_len  host-side bound on the lengths.
- *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes.  Nothing
- *                 in it is read before this call writes it; concurrent calls must not share one.
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...) bytes, 256-byte
+ *                 aligned (hipMalloc'd memory is).  Nothing in it is read before this call
+ *                 writes it; concurrent calls must not share one.
  * The batch's (sequence, kv head, frame) work is split into equal contiguous ranges over a
  * fixed set of persistent wavefronts; a sequence cut by a range boundary is merged from
  * partial results by a second (reduce) kernel, exactly up to fp32 rounding ("CUDA Shared
@@ -185,7 +186,7 @@ size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max
  *   query_start_loc  int32 [num_chunks + 1], non-decreasing, starting at 0.
  *   context_lens     int32 [num_chunks], C_c <= L_c <= max_context_len.
  *   max_chunk_len    host-side bound on C_c; sizes the grid together with max_context_len.
- *   workspace        at least pa_prefill_chunk_workspace_bytes(...) bytes.
+ *   workspace        at least pa_prefill_chunk_workspace_bytes(...) bytes, 256-byte aligned.
  * The chunk's own K/V must already be in the cache (pa_reshape_and_cache on the same
  * stream).
  */
@@ -229,8 +230,8 @@ size_t pa_mixed_workspace_bytes(int num_decodes, int num_chunks, int64_t total_q
  *   flags            PA_DECODE_SHARED_FRAMES as for pa_decode_ex (decode loads only);
  *                    PA_MIXED_SPLIT or PA_MIXED_SEPARATE force the mode (below) instead of
  *                    the host's choice (for tuning and tests; results agree either way).
- *   workspace        at least pa_mixed_workspace_bytes(...) bytes; concurrent calls must not
- *                    share one.
+ *   workspace        at least pa_mixed_workspace_bytes(...) bytes, 256-byte aligned;
+ *                    concurrent calls must not share one.
  * Every K/V the step attends (the chunks' own rows and the decodes' new tokens) must already be
  * in the cache (pa_reshape_and_cache on the same stream).  Outputs match pa_decode and
  * pa_prefill_chunk to fp32 rounding (the context splits differ); equal inputs and decode_tokens

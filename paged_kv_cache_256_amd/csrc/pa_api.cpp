@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <atomic>
+#include <cstdint>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -179,6 +180,8 @@ int pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_ca
   const size_t need = pa::decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)workspace & 255u))
+    return fail(PA_EINVAL, "workspace must be 256-byte aligned");
   pa::DecodeParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
                      B, Hq, Hkv, D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
                      max_context_len, need > 0 ? workspace : nullptr,
@@ -231,6 +234,8 @@ int pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* 
   const size_t need = pa::prefill_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv, D, (int)kv_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)workspace & 255u))
+    return fail(PA_EINVAL, "workspace must be 256-byte aligned");
   pa::PrefillParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, query_start_loc,
                       context_lens, num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,
                       D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
@@ -332,6 +337,8 @@ int pa_mixed_attention(void* out, const void* q, const void* k_cache, const void
                                                 max_context_len, Hq, Hkv, D, (int)kv_dtype);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)workspace & 255u))
+    return fail(PA_EINVAL, "workspace must be 256-byte aligned");
   pa::MixedParams p = mixed_params(num_decodes, num_chunks, total_q, max_chunk_len,
                                    max_context_len, decode_tokens, Hq, Hkv, D, block_size, kv_dtype);
   p.out = out;

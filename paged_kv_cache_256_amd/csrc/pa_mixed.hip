@@ -212,7 +212,7 @@ MixedLayout mixed_layout(int num_decodes, int num_chunks, long long crows, int m
   if (num_chunks > 0 && crows > 0) {
     l.nsplit_max = choose_split(num_chunks, max_chunk_len, max_context_len, Hq, Hkv,
                                 kind_of(kv_dtype), device_compute_units()).nsplit;
-    if (l.nsplit_max > 1) l.pre_bytes = (size_t)crows * Hq * l.nsplit_max * (2 + (size_t)D) * sizeof(float);
+    if (l.nsplit_max > 1) l.pre_bytes = partial_bytes(crows * Hq, l.nsplit_max, D);
   }
   return l;
 }
@@ -272,7 +272,7 @@ hipError_t launch_mixed_typed(const MixedParams& p, hipStream_t stream) {
   const long long crows = chunk_rows(p);
   const bool psplit = has_c && roles.sp.nsplit > 1;
   a.p_ml = psplit ? (float*)(ws + ml.dec_bytes) : nullptr;
-  a.p_o = psplit ? a.p_ml + (size_t)2 * crows * p.Hq * roles.sp.nsplit : nullptr;
+  a.p_o = psplit ? a.p_ml + partial_ml_floats(crows * p.Hq, roles.sp.nsplit) : nullptr;
   a.nc = p.num_chunks;
   const int G = p.Hq / p.Hkv;
   const int TQ = kPWaves * tiles_per_wave(KIND) * 16 / G;
@@ -324,7 +324,7 @@ hipError_t launch_mixed_typed(const MixedParams& p, hipStream_t stream) {
   m.Hkv = p.Hkv;
   m.G = G;
   m.v_scale = a.v_scale;
-  const long long pblocks = psplit ? (crows * p.Hq + 3) / 4 : 0;
+  const long long pblocks = psplit ? (crows * p.Hq + 7) / 8 : 0;
   const long long blocks = m.dblocks + pblocks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((mixed_merge_kernel<KIND, D>), dim3((unsigned)blocks), dim3(256), 0, stream, m);

@@ -64,7 +64,7 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   const int TQ = kPWaves * NT * 16 / G;
   float* ws_ml = (float*)p.workspace;
   const long long rows = p.total_q - p.row_base;  // rows of the chunks
-  float* ws_o = ws_ml ? ws_ml + (size_t)2 * rows * p.Hq * sp.nsplit : nullptr;
+  float* ws_o = ws_ml ? ws_ml + partial_ml_floats(rows * p.Hq, sp.nsplit) : nullptr;
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
   dim3 grid(sp.nsplit, (p.max_chunk_len + TQ - 1) / TQ, p.num_chunks * p.Hkv);
@@ -79,7 +79,7 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
                                                                  : p.max_blocks_per_seq * BS;
   const long long pairs = rows * p.Hq;
-  hipLaunchKernelGGL((prefill_reduce_kernel<KIND, D>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0,
+  hipLaunchKernelGGL((prefill_reduce_kernel<KIND, D>), dim3((unsigned)((pairs + 7) / 8)), dim3(256), 0,
                      stream, p.out, ws_ml, ws_o, p.query_start_loc, p.context_lens, p.num_chunks,
                      (long long)p.total_q, (long long)p.row_base, p.Hq, sp.nsplit, sp.KS, cap,
                      v_scale);
@@ -105,7 +105,7 @@ size_t prefill_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_le
   const Split sp = choose_split(num_chunks, max_chunk_len, max_context_len, Hq, Hkv, kind,
                                 device_compute_units());
   if (sp.nsplit <= 1) return 0;
-  return (size_t)total_q * Hq * sp.nsplit * (2 + (size_t)D) * sizeof(float);
+  return partial_bytes(total_q * Hq, sp.nsplit, D);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {

@@ -362,16 +362,21 @@ __device__ __forceinline__ void prefill_tile(
 }
 
 // Merge the context splits of every (row, head) whose keys span more than one split:
-// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.  One wavefront per
-// (row, head), four per workgroup; lane l merges head-dim elements [l*NV, (l+1)*NV).  All of a
-// row's partials are loaded before any is used.
+// out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, M = max_p m_p.  Each half of a wavefront
+// takes one (row, head) pair (wavefront wv: pairs 2 wv and 2 wv + 1), so that every pair of a
+// chunk is in flight at once; lane l of the half merges head-dim elements [l NV, (l+1) NV)
+// with 16- (or 8-) byte loads.  kBatch partials of a pair are loaded before any is used.
 template <int KIND, int D>
 __device__ __forceinline__ void prefill_reduce_wave(
-    long long pair, int lane, long long row_base, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens, int num_chunks,
-    long long total_q, int Hq, int nsplit, int KS, int cap, float v_scale) {
-  constexpr int NV = D / 64;       // outputs per lane
-  constexpr int kMaxSplit = 16;    // partials held in registers at once
+    long long wv, int lane, long long row_base, void* __restrict__ out, const float* __restrict__ ws_ml,
+    const float* __restrict__ ws_o, const int32_t* __restrict__ qsl,
+    const int32_t* __restrict__ context_lens, int num_chunks, long long total_q, int Hq, int nsplit,
+    int KS, int cap, float v_scale) {
+  constexpr int NV = D / 32;   // outputs per lane (4 or 2)
+  constexpr int kBatch = 4;    // partials held in registers at once
+  typedef float fv __attribute__((ext_vector_type(NV)));
+  const long long pair = 2 * wv + (lane >> 5);
+  const int l = lane & 31;
   if (pair >= (total_q - row_base) * Hq) return;
   const long long r = row_base + pair / Hq;
   const int h = (int)(pair % Hq);
@@ -388,51 +393,55 @@ __device__ __forceinline__ void prefill_reduce_wave(
   const int nsp = min(nsplit, pos / KS + 1);
   if (nsp <= 1) return;
   const size_t base = (size_t)pair * nsplit;
-  float M = -INFINITY, den = 0.f, num[NV];
+  float M = -INFINITY, den = 0.f;
+  fv num = (fv)0.f;
+  for (int p0 = 0; p0 < nsp; p0 += kBatch) {
+    float mp[kBatch], lp[kBatch];
+    fv op[kBatch];
 #pragma unroll
-  for (int v = 0; v < NV; ++v) num[v] = 0.f;
-  for (int p0 = 0; p0 < nsp; p0 += kMaxSplit) {
-    float mp[kMaxSplit], lp[kMaxSplit], op[kMaxSplit][NV];
-#pragma unroll
-    for (int i = 0; i < kMaxSplit; ++i) {
+    for (int i = 0; i < kBatch; ++i) {
       const bool has = p0 + i < nsp;
       const size_t q = base + (has ? p0 + i : 0);
       mp[i] = has ? ws_ml[2 * q] : -INFINITY;
       lp[i] = has ? ws_ml[2 * q + 1] : 0.f;
-#pragma unroll
-      for (int v = 0; v < NV; ++v) op[i][v] = has ? ws_o[q * D + lane * NV + v] : 0.f;
+      op[i] = has ? *(const fv*)(ws_o + q * D + l * NV) : (fv)0.f;
     }
 #pragma unroll
-    for (int i = 0; i < kMaxSplit; ++i) {
+    for (int i = 0; i < kBatch; ++i) {
       if (mp[i] == -INFINITY) continue;
       if (mp[i] > M) {
         const float sc = __builtin_amdgcn_exp2f(M - mp[i]);
         den *= sc;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) num[v] *= sc;
+        num *= sc;
         M = mp[i];
       }
       const float e = __builtin_amdgcn_exp2f(mp[i] - M);
       den += e * lp[i];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) num[v] += e * op[i][v];
+      num += e * op[i];
     }
   }
-  const size_t o = ((size_t)r * Hq + h) * D + lane * NV;
+  const size_t o = ((size_t)r * Hq + h) * D + l * NV;
+  const fv x = num / den * v_scale;
+  if constexpr (KIND == KF32) {
+    *(fv*)((float*)out + o) = x;
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const float x = num[v] / den * v_scale;
-    if constexpr (KIND == KF32) {
-      ((float*)out)[o + v] = x;
-    } else {
-      ((__bf16*)out)[o + v] = (__bf16)x;
-    }
+    for (int v = 0; v < NV; v += 2) *(uint32_t*)((__bf16*)out + o + v) = pack_bf16x2(x[v], x[v + 1]);
   }
 }
 
 struct Split {
   int nsplit, KS;
 };
+
+// Split partials of `pairs` (row, head) pairs over nsplit ranges: the (max, sum) pairs, then the
+// accumulator rows from a 16-byte boundary.
+inline size_t partial_ml_floats(long long pairs, int nsplit) {
+  return ((size_t)2 * pairs * nsplit + 3) / 4 * 4;
+}
+inline size_t partial_bytes(long long pairs, int nsplit, int D) {
+  return (partial_ml_floats(pairs, nsplit) + (size_t)pairs * nsplit * D) * sizeof(float);
+}
 
 // Context split of a launch that aims for `target` workgroups: nsplit key ranges of KS keys
 // (a multiple of 64, at least 256 keys per range unless the context is shorter).

@@ -365,3 +365,16 @@ def test_prepared_calls_need_their_buffers_passed_in():
     with pytest.raises(ValueError, match="out"):
         pa.prefill_chunk(None, None, None, None, None, None, block_size=16, scale=0.1,
                          kv_dtype="bf16", max_chunk_len=16, max_context_len=16, prepared=True)
+
+
+def test_workspaces_must_be_256_byte_aligned():
+    odd = ctypes.c_void_p(0x1010)
+    f = lib().pa_decode_ex
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 8, 2, 128, 16, 64, 0.1, BF16, BF16, 1.0, 1.0,
+            128]
+    assert f(*args, odd, 1 << 40, 0, NULL) == EINVAL and "aligned" in err()
+    assert mixed(ws=odd, wsb=1 << 40) == EINVAL and "aligned" in err()
+    need = lib().pa_prefill_chunk_workspace_bytes(1, 512, 512, 16384, 32, 8, 128, 16, BF16)
+    assert need > 0
+    assert prefill(nc=1, tq=512, mcl=512, mctx=16384, Hq=32, Hkv=8, D=128, ws=odd,
+                   wsb=need) == EINVAL and "aligned" in err()
