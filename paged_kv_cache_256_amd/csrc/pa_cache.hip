@@ -3,8 +3,9 @@
 // reshape_and_cache follows the block-table mapping of codebumble.net ("The Block Table
 // Mapping Subsystem"): a token's slot names its frame (slot / block_size) and its offset in
 // the frame (slot % block_size).  Each workgroup stores one token: every KV head's D values
-// go to their places in the (frame, head) tile of the operand-order layout.  An fp8 cache
-// stores e4m3fn(fp32(x) / scale), rounded to nearest even with saturation.
+// go to their places in the (frame, head) tile of the operand-order layout (16-byte stores for
+// K, element stores for V).  An fp8 cache stores e4m3fn(fp32(x) / scale), rounded to nearest
+// even with saturation.
 //
 // copy_blocks implements the copy half of copy-on-write (infoisland, section 2): a frame
 // shared by several sequences is duplicated before one of them writes into it.
@@ -16,6 +17,11 @@ namespace pa {
 
 namespace {
 
+// One workgroup per token.  Thread t takes one 16-byte piece of the token's K row in the tile
+// layout (EPC = 16 / element-bytes consecutive head-dim values of one KV head, contiguous in the
+// K tile since a lane's fragment holds consecutive head-dim values of one key) and stores it
+// with one 16-byte store; the same head-dim values of V sit in EPC different fragments of the
+// V tile (there a fragment holds consecutive keys) and are stored one by one.
 template <int SRC, int KV, int D, int BS>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     const void* __restrict__ k, const void* __restrict__ v, char* __restrict__ k_cache,
@@ -23,35 +29,43 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     float k_scale, float v_scale) {
   constexpr int EB = KV == KF32 ? 4 : (KV == KBF16 ? 2 : 1);
   constexpr int TILE = BS * D * EB;
+  constexpr int EPC = 16 / EB;  // elements per 16-byte piece
+  static_assert((D / 4) % EPC == 0, "a piece must not cross a fragment");
   const long long i = blockIdx.x;
   const long long s = slots[i];
   if (s < 0 || s >= NB * BS) return;
   const long long f = s / BS;
   const int o = (int)(s % BS);
-  for (int idx = threadIdx.x; idx < Hkv * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx % D;
-    const size_t src = ((size_t)i * Hkv + g) * D + d;
+  for (int pc = threadIdx.x; pc < Hkv * (D / EPC); pc += blockDim.x) {
+    const int g = pc / (D / EPC), d0 = (pc % (D / EPC)) * EPC;
+    const size_t src = ((size_t)i * Hkv + g) * D + d0;
     const size_t tile = ((size_t)f * Hkv + g) * TILE;
-    char* kd = k_cache + tile + k_tile_byte(o, d, D, EB);
-    char* vd = v_cache + tile + v_tile_byte(o, d, D, EB);
-    if constexpr (KV == KF32) {
-      *(uint32_t*)kd = ((const uint32_t*)k)[src];
-      *(uint32_t*)vd = ((const uint32_t*)v)[src];
-    } else if constexpr (KV == KBF16) {
-      *(uint16_t*)kd = ((const uint16_t*)k)[src];
-      *(uint16_t*)vd = ((const uint16_t*)v)[src];
-    } else {
-      float xk, xv;
-      if constexpr (SRC == KF32) {
-        xk = ((const float*)k)[src];
-        xv = ((const float*)v)[src];
+    u32x4 kp;
+    uint8_t* kb = (uint8_t*)&kp;
+    char* vd = v_cache + tile;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      char* vdst = vd + v_tile_byte(o, d0 + e, D, EB);
+      if constexpr (KV == KF32) {
+        ((uint32_t*)kb)[e] = ((const uint32_t*)k)[src + e];
+        *(uint32_t*)vdst = ((const uint32_t*)v)[src + e];
+      } else if constexpr (KV == KBF16) {
+        ((uint16_t*)kb)[e] = ((const uint16_t*)k)[src + e];
+        *(uint16_t*)vdst = ((const uint16_t*)v)[src + e];
       } else {
-        xk = __uint_as_float((uint32_t)((const uint16_t*)k)[src] << 16);
-        xv = __uint_as_float((uint32_t)((const uint16_t*)v)[src] << 16);
+        float xk, xv;
+        if constexpr (SRC == KF32) {
+          xk = ((const float*)k)[src + e];
+          xv = ((const float*)v)[src + e];
+        } else {
+          xk = __uint_as_float((uint32_t)((const uint16_t*)k)[src + e] << 16);
+          xv = __uint_as_float((uint32_t)((const uint16_t*)v)[src + e] << 16);
+        }
+        kb[e] = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xk, k_scale));
+        *(uint8_t*)vdst = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xv, v_scale));
       }
-      *(uint8_t*)kd = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xk, k_scale));
-      *(uint8_t*)vd = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xv, v_scale));
     }
+    *(u32x4*)(k_cache + tile + k_tile_byte(o, d0, D, EB)) = kp;
   }
 }
 
