@@ -226,7 +226,13 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run three plain device copies of this many MiB before the timed steps "
                          "(a known-size reference for hardware byte counters)")
+    ap.add_argument("--block-manager", action="store_true",
+                    help="time the host block manager (no GPU): prompts, decode steps with their "
+                         "block-table export, and copy-on-write forks, for the 70B-shape batch")
     args = ap.parse_args()
+    if args.block_manager:
+        block_manager_bench()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
         sys.exit(2)
@@ -414,6 +420,77 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def block_manager_bench():
+    """Host-side rows of the path (the block manager): time the library's pa_bm_* calls on the
+    70B-shape batch (256 sequences, prompts log-uniform in [128, 8192], 16-token blocks) and the
+    plain-Python reference model on the same operations.  One JSON line."""
+    import paged_kv_cache_256_amd as pa
+    from oracle.block_manager import BlockManagerModel
+
+    rng = np.random.default_rng(3)
+    B, bs, steps = 256, 16, 200
+    lens = np.clip(np.round(np.exp(rng.uniform(np.log(128), np.log(8192), B))), 128, 8192).astype(int)
+    frames = int(sum(-(-(L + steps) // bs) for L in lens)) * 2 + 64
+    prompts = [rng.integers(0, 32000, size=L).astype(np.int32) for L in lens]
+    width = -(-(int(lens.max()) + steps) // bs)
+    ids = np.arange(B, dtype=np.int64)
+
+    def run(bm, n_steps, export):
+        t0 = time.perf_counter()
+        for b in range(B):
+            bm.append_prompt(b, prompts[b])
+        t1 = time.perf_counter()
+        for _ in range(n_steps):
+            bm.append(ids)
+            if export:
+                bm.block_tables(ids, width)
+        t2 = time.perf_counter()
+        return t1 - t0, (t2 - t1) / n_steps
+
+    bm = pa.BlockManager(frames, bs)
+    lib_prompt_s, lib_step_s = run(bm, steps, True)
+    # copy-on-write: fork every sequence and append one token to each branch
+    t0 = time.perf_counter()
+    for b in range(B):
+        bm.fork(b, B + b)
+    _, pairs = bm.append(np.arange(B, 2 * B, dtype=np.int64))
+    lib_fork_s = time.perf_counter() - t0
+    bm.close()
+
+    class ModelAdapter:
+        def __init__(self):
+            self.m = BlockManagerModel(frames, bs)
+
+        def append_prompt(self, seq, toks):
+            self.m.append_prompt(seq, toks)
+
+        def append(self, seq_ids):
+            self.m.append(seq_ids)
+
+        def block_tables(self, seq_ids, w):
+            return [self.m.block_table(int(s), w) for s in seq_ids]
+
+    model_steps = 5
+    model_prompt_s, model_step_s = run(ModelAdapter(), model_steps, True)
+    tokens = int(lens.sum())
+    line = {
+        "metric": "host block manager: one decode step of 256 sequences (append + block-table export)",
+        "value": round(lib_step_s * 1e6, 1), "unit": "us", "higher_is_better": False,
+        "data": "synthetic (seeded prompt token ids)",
+        "config": {"workload": "70B-shape batch: 256 sequences, prompts log-uniform in [128, 8192], bs 16",
+                   "frames": frames, "prompt_tokens": tokens, "decode_steps": steps,
+                   "prompts_us": round(lib_prompt_s * 1e6, 1),
+                   "prompt_tokens_per_s": round(tokens / lib_prompt_s, 1),
+                   "fork_and_cow_append_us": round(lib_fork_s * 1e6, 1),
+                   "cow_copies": int(len(pairs))},
+        "cpu_baseline": {"value": round(model_step_s * 1e6, 1), "unit": "us", "cores": 1,
+                         "kind": "oracle",
+                         "sample": f"the reference model on the same prompts and {model_steps} decode steps",
+                         "prompts_us": round(model_prompt_s * 1e6, 1)},
     }
     print(json.dumps(line), flush=True)
 

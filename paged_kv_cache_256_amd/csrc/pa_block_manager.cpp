@@ -23,6 +23,7 @@
 //    can revive it) and loses it when allocation reuses the frame.
 // Every mutating call either succeeds completely or changes nothing.
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <deque>
@@ -169,8 +170,15 @@ int pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int64_t n, int64_
   if (n == 0) return pa::clear_error();
   // Pass 1 (no state change): frames needed, with the reference counts and lengths each
   // entry would see after the earlier entries of the same call.
+  // A sequence is summarised by its length and last frame (-1: a fresh frame of this call,
+  // referenced once); only those change within one call.
+  struct Tail {
+    int64_t len;
+    int32_t last;
+  };
   std::unordered_map<int32_t, int32_t> ref_delta;
-  std::unordered_map<int64_t, pa_block_manager::Seq> touched;
+  std::unordered_map<int64_t, Tail> touched;
+  touched.reserve((size_t)n);
   int64_t need = 0;
   auto ref_of = [&](int32_t f) {
     auto it = ref_delta.find(f);
@@ -181,20 +189,21 @@ int pa_bm_append(pa_block_manager* bm, const int64_t* seq_ids, int64_t n, int64_
     auto t = touched.find(id);
     if (t == touched.end()) {
       auto it = bm->seqs.find(id);
-      t = touched.emplace(id, it == bm->seqs.end() ? pa_block_manager::Seq{} : it->second).first;
-    }
-    pa_block_manager::Seq& s = t->second;
-    const int64_t off = s.len % bm->bs;
-    if (off == 0) {
-      ++need;
-      s.frames.push_back(-1);  // placeholder: a fresh frame, referenced once
-    } else {
-      const int32_t last = s.frames.back();
-      if (last >= 0 && ref_of(last) > 1) {
-        ++need;
-        --ref_delta[last];
-        s.frames.back() = -1;
+      Tail tl{0, -1};
+      if (it != bm->seqs.end()) {
+        tl.len = it->second.len;
+        tl.last = it->second.frames.empty() ? -1 : it->second.frames.back();
       }
+      t = touched.emplace(id, tl).first;
+    }
+    Tail& s = t->second;
+    if (s.len % bm->bs == 0) {
+      ++need;
+      s.last = -1;  // a fresh frame, referenced once
+    } else if (s.last >= 0 && ref_of(s.last) > 1) {
+      ++need;
+      --ref_delta[s.last];
+      s.last = -1;
     }
     ++s.len;
   }
@@ -341,7 +350,9 @@ int pa_bm_block_tables(const pa_block_manager* bm, const int64_t* seq_ids, int64
   for (int64_t i = 0; i < n; ++i) {
     const pa_block_manager::Seq& s = bm->seqs.find(seq_ids[i])->second;
     int32_t* row = tables + (size_t)i * max_blocks_per_seq;
-    for (int k = 0; k < max_blocks_per_seq; ++k) row[k] = k < (int)s.frames.size() ? s.frames[k] : -1;
+    const size_t k = s.frames.size();
+    std::copy(s.frames.begin(), s.frames.end(), row);
+    std::fill(row + k, row + max_blocks_per_seq, -1);
     context_lens[i] = (int32_t)s.len;
   }
   return pa::clear_error();

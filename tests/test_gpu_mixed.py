@@ -101,18 +101,19 @@ def test_mixed_every_mode_and_hint_is_correct_and_repeat_is_bit_identical():
     assert len(units) >= 3, f"modes and hints should give different launches, got {units}"
 
 
-def test_mixed_plan_kernel_path_above_1024_decodes():
+@pytest.mark.parametrize("mode", ["split", "separate"])
+def test_mixed_plan_kernel_path_above_1024_decodes(mode):
     rng = np.random.default_rng(5)
     lens = rng.integers(1, 300, size=1100)
     c = workloads.chunk_case("mixed-big", 43, Hq=8, Hkv=2, D=64, bs=16, chunks=[(256, 1024)],
                              decode_lens=lens, kv_dtype="bf16", std=0.7071)
     g, o = GpuStep(c), OracleStep(c)
     g.write()
-    d, ch = g.mixed()
+    d, ch = g.mixed(mode=mode)
     torch.cuda.synchronize()
     seqs = sorted(set(rng.choice(c.B, size=120, replace=False).tolist()) | {0, c.B - 1})
     err = _check(g, o, d, ch, decode_seqs=seqs)
-    _say(f"  1100 decodes + chunk: max abs err {err:.2e}")
+    _say(f"  1100 decodes + chunk ({mode}): max abs err {err:.2e}")
 
 
 def test_mixed_matches_separate_calls_within_tolerance():
