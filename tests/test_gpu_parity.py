@@ -86,6 +86,8 @@ CHUNK_CASES = [
     ("bf16", 64, 16, 16, [(33, 33), (70, 500)], [20]),
     ("bf16", 128, 16, 1, [(130, 900)], []),
     ("fp8", 128, 32, 4, [(200, 1000)], [77]),
+    # a short chunk deep into a long prompt: the context splits into ~128 ranges per tile
+    ("bf16", 128, 16, 1, [(16, 40000)], [3]),
 ]
 
 
