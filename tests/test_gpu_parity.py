@@ -300,8 +300,9 @@ def test_decode_stream_split_extremes(name, Hq, Hkv, kv, bs, lens):
 
 
 def test_graph_replays_match_eager_bits():
-    """A step captured in a HIP graph (copies, cache writes, prefill chunk, decode) and replayed
-    several times, with eager work between the replays, gives the eager step's bits each time."""
+    """A step captured in a HIP graph (copies, cache writes, prefill chunk, decode, and the mixed
+    step in its single-kernel mode) and replayed several times, with eager work between the
+    replays, gives the eager step's bits each time."""
     _say("graph replay case")
     c = workloads.fork_case("graph-fork", 11, prompts=3, branches=3, prompt_len=320, tail_lo=1,
                             tail_hi=60, Hq=16, Hkv=2, D=128, bs=16, kv_dtype="bf16")
@@ -315,6 +316,8 @@ def test_graph_replays_match_eager_bits():
                                                c.max_context_len), dtype=torch.uint8, device=dev)
     out = torch.empty_like(g.q)
     cout = torch.empty_like(h.cq)
+    mout = torch.empty((h.c.B + h.cq.shape[0],) + tuple(h.cq.shape[1:]), dtype=h.cq.dtype,
+                       device=dev)
 
     def step():
         g.write()
@@ -322,10 +325,12 @@ def test_graph_replays_match_eager_bits():
         h.write()
         h.prefill()
         cout.copy_(h.chunk_out)
+        h.mixed(mode="split")
+        mout.copy_(h.mixed_out)
 
     step()
     torch.cuda.synchronize()
-    want, cwant = out.clone(), cout.clone()
+    want, cwant, mwant = out.clone(), cout.clone(), mout.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -339,6 +344,7 @@ def test_graph_replays_match_eager_bits():
     for r in range(4):
         out.zero_()
         cout.zero_()
+        mout.zero_()
         # eager work between the replays: another decode into a fresh buffer
         g.decode()
         torch.cuda.synchronize()
@@ -346,6 +352,7 @@ def test_graph_replays_match_eager_bits():
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"decode, replay {r}"
         assert torch.equal(cout.view(torch.int16), cwant.view(torch.int16)), f"prefill, replay {r}"
+        assert torch.equal(mout.view(torch.int16), mwant.view(torch.int16)), f"mixed, replay {r}"
     o = OracleStep(c)
     err = np.abs(out_f64(out) - o.decode()).max()
     assert err <= tolerance(c)
