@@ -36,7 +36,7 @@ class PAError(RuntimeError):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_256_amd.build`"
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_256_amd/build.py`"
                       " (there is no fallback implementation)")
 
 _lib = ctypes.CDLL(LIB_PATH)

@@ -1,6 +1,7 @@
 """Build libpa.so (the paged-attention HIP library for gfx950) in place.
 
-Usage: python -m paged_kv_cache_256_amd.build [-v]
+Usage: python paged_kv_cache_256_amd/build.py [-v]
+(run as a script: the package itself does not import until libpa.so exists)
 
 Every HIP source is compiled with hipcc for gfx950 only; the objects go to _build/ at the
 repository root and the shared library to paged_kv_cache_256_amd/libpa.so, next to the
