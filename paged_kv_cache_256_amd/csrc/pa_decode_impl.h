@@ -167,17 +167,19 @@ __device__ __forceinline__ void decode_stream_wave(
   uint64_t live_mask = 0;
   int L = 0, cblk = 0;  // context length and first block of the current chunk
 
-  auto load_step = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s) {
+  // Gather step s of a chunk whose frame ids (one per lane) and lane strides are fid / fstride,
+  // for kv head gg.
+  auto load_step = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s, int fid, int fstride, int gg) {
     // keep a step's loads together and in order: the in-order load counter then lets the
     // compute of the previous step wait for exactly its own data
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int i = min(s * F + f, 63);
-      const int fr = __builtin_amdgcn_readlane(vfid, i);
-      const int ls = lane * __builtin_amdgcn_readlane(vstride, i);
-      const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
-      const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + g) * TILE) + ls;
+      const int fr = __builtin_amdgcn_readlane(fid, i);
+      const int ls = lane * __builtin_amdgcn_readlane(fstride, i);
+      const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + gg) * TILE) + ls;
+      const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + gg) * TILE) + ls;
 #pragma unroll
       for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16<NT>(kp + r * 64);
 #pragma unroll
@@ -250,89 +252,174 @@ __device__ __forceinline__ void decode_stream_wave(
     }
   };
 
-  u32x4 kA[F][NL], vA[F][NL], kB[F][NL], vB[F][NL];
-  long long x = a;
-  while (x < e && b < B) {
-    L = max(0, min(context_lens[b], cap));
-    const int nblk = (L + BS - 1) / BS;
-    const int units = (int)min((long long)(run_units(nblk) - u), e - x);  // of this run, here
-    // frames of the run inside this wavefront's range (its first kRestart units hold none)
-    const int f0 = max(0, u - kRestart), f1 = min(nblk, u + units - kRestart);
-    const int n_here = f1 - f0;
-    if (n_here > 0) {
-      const long long s0 = x - u;  // first unit of this (b, g) run
-      const bool complete = f0 == 0 && f1 == nblk;
-      const int blk = f0;
-      // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G)
-      {
-        const bool qv = n < G;
-        const size_t row = (size_t)b * Hq + (size_t)g * G + (qv ? n : 0);
-        const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
+  // The wavefront's frames are visited as chunks of up to kIds consecutive frames of one run
+  // piece (the frames of a (sequence, kv head) run that lie in this wavefront's range).  The tile
+  // pipeline runs on across chunk and run boundaries: while a chunk is computed, the block ids
+  // and the query of the next chunk are fetched, and the chunk's last two load steps gather the
+  // next chunk's first two steps (in place of loads past the chunk), so the wavefront keeps two
+  // steps of tiles in flight from its first frame to its last.
+  struct Piece {
+    int b, g, L, nblk, f0, n, slot;
+    bool complete;
+  };
+  long long x = a;  // first unit of the next run to look at
+  int rb = b, rg = g, ru = u;
+  // The next run piece with frames in [x, e), or false past the end of the range.
+  auto find_piece = [&](Piece& pc) -> bool {
+    while (x < e && rb < B) {
+      const int Lr = max(0, min(context_lens[rb], cap));
+      const int nb = (Lr + BS - 1) / BS;
+      const int units = (int)min((long long)(run_units(nb) - ru), e - x);
+      // frames of the run inside this wavefront's range (its first kRestart units hold none)
+      const int f0 = max(0, ru - kRestart), f1 = min(nb, ru + units - kRestart);
+      const long long s0 = x - ru;  // first unit of this (b, g) run
+      const int pb = rb, pg = rg;
+      x += units > 0 ? units : 0;
+      ru = 0;
+      if (++rg == Hkv) {
+        rg = 0;
+        ++rb;
+      }
+      if (f1 > f0) {
+        pc.b = pb;
+        pc.g = pg;
+        pc.L = Lr;
+        pc.nblk = nb;
+        pc.f0 = f0;
+        pc.n = f1 - f0;
+        pc.complete = f0 == 0 && f1 == nb;
+        pc.slot = s0 > a ? 1 : 0;
+        return true;
+      }
+    }
+    return false;
+  };
+  // Raw block id of lane `lane` of chunk c0 of piece pc (clamped to the run's last block).
+  auto chunk_id = [&](const Piece& pc, int c0) {
+    return block_tables[(size_t)pc.b * mbps + min(pc.f0 + c0 + lane, pc.nblk - 1)];
+  };
+  // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G)
+  auto load_q = [&](uint32_t (&dst)[QW], const Piece& pc) {
+    const bool qv = n < G;
+    const size_t row = (size_t)pc.b * Hq + (size_t)pc.g * G + (qv ? n : 0);
+    const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
 #pragma unroll
-        for (int i = 0; i < QW / 4; ++i) {
-          u32x4 v4 = src[i];
-          if (!qv) v4 = (u32x4){0u, 0u, 0u, 0u};
-          qw[4 * i] = v4[0]; qw[4 * i + 1] = v4[1]; qw[4 * i + 2] = v4[2]; qw[4 * i + 3] = v4[3];
+    for (int i = 0; i < QW / 4; ++i) {
+      u32x4 v4 = src[i];
+      if (!qv) v4 = (u32x4){0u, 0u, 0u, 0u};
+      dst[4 * i] = v4[0]; dst[4 * i + 1] = v4[1]; dst[4 * i + 2] = v4[2]; dst[4 * i + 3] = v4[3];
+    }
+  };
+  // ids of a chunk: live lanes (inside the chunk, valid id) load their frame, dead ones read the
+  // same 16 bytes of frame 0 (stride 0)
+  auto resolve = [&](int f_raw, int cn, bool any, int& fid, int& fstride, uint64_t& mask) {
+    const bool ok = any && lane < cn && f_raw >= 0 && (long long)f_raw < NB;
+    mask = __ballot(ok);
+    fid = ok ? f_raw : 0;
+    fstride = ok ? 1 : 0;
+  };
+  auto finalize = [&](const Piece& pc) {
+    const float lrow = wave_sum_over_j(lsum);
+    if (n < G) {
+      if (pc.complete) {
+        const float inv = v_scale / lrow;
+        const size_t o = ((size_t)pc.b * Hq + (size_t)pc.g * G + n) * D + 4 * j;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          if constexpr (KIND == KF32) {
+            *(f32x4*)((float*)out + o + 16 * c) = acc[c] * inv;
+          } else {
+            u32x2 pk;
+            pk[0] = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
+            pk[1] = pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv);
+            *(u32x2*)((__bf16*)out + o + 16 * c) = pk;
+          }
+        }
+      } else {
+        const size_t row = ((size_t)w * 2 + pc.slot) * 16 + n;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) *(f32x4*)(ws_o + row * D + 16 * c + 4 * j) = acc[c];
+        if (j == 0) {
+          ws_ml[2 * row] = m;
+          ws_ml[2 * row + 1] = lrow;
         }
       }
+    }
+  };
+
+  Piece pc;
+  if (!find_piece(pc)) return;
+  int c0 = 0;  // first frame of the current chunk within its piece
+  L = pc.L;
+  cblk = pc.f0;
+  resolve(chunk_id(pc, 0), min(kIds, pc.n), true, vfid, vstride, live_mask);
+  load_q(qw, pc);
+  m = -INFINITY;
+  lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  u32x4 kA[F][NL], vA[F][NL], kB[F][NL], vB[F][NL];
+  load_step(kA, vA, 0, vfid, vstride, pc.g);
+  load_step(kB, vB, 1, vfid, vstride, pc.g);
+  // the next chunk's query is prefetched unless its fragment is large (f32 with D = 128: a second
+  // copy would not fit the register budget)
+  constexpr bool kPrefetchQ = QW <= 16;
+  uint32_t qn[QW];
+  for (;;) {
+    // the next chunk: the rest of this piece, or the next piece
+    Piece pn = pc;
+    int c0n = c0 + kIds;
+    bool more = c0n < pc.n;
+    if (!more) {
+      c0n = 0;
+      more = find_piece(pn);
+    }
+    // its raw ids and query, fetched now and used at the end of this chunk
+    int f_raw_n = 0;
+    if (more) f_raw_n = chunk_id(pn, c0n);
+    if constexpr (kPrefetchQ) load_q(qn, pn);
+    const int cnn = more ? min(kIds, pn.n - c0n) : 0;
+    const int cn = min(kIds, pc.n - c0);
+    const int np = (cn + 2 * F - 1) / (2 * F) * 2;  // steps of the chunk, an even count
+    int vfid_n = 0, vstride_n = 0;
+    uint64_t live_n = 0;
+    // load step s2 of this chunk, or step s2 - np of the next one
+    auto load_next = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s2) {
+      const bool nx = s2 >= np;
+      load_step(kt, vt, nx ? s2 - np : s2, nx ? vfid_n : vfid, nx ? vstride_n : vstride,
+                nx ? pn.g : pc.g);
+    };
+    for (int s = 0; s < np; s += 2) {
+      compute_step(kA, vA, s);
+      if (s + 2 >= np) resolve(f_raw_n, cnn, more, vfid_n, vstride_n, live_n);
+      load_next(kA, vA, s + 2);
+      compute_step(kB, vB, s + 1);
+      load_next(kB, vB, s + 3);
+    }
+    if (c0 + kIds >= pc.n) finalize(pc);
+    if (!more) break;
+    const bool fresh = c0n == 0;
+    pc = pn;
+    c0 = c0n;
+    L = pc.L;
+    cblk = pc.f0 + c0;
+    vfid = vfid_n;
+    vstride = vstride_n;
+    live_mask = live_n;
+    if constexpr (kPrefetchQ) {
+#pragma unroll
+      for (int i = 0; i < QW; ++i) qw[i] = qn[i];
+    } else {
+      load_q(qw, pc);
+    }
+    if (fresh) {
       m = -INFINITY;
       lsum = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-      for (int c0 = 0; c0 < n_here; c0 += kIds) {
-        const int cn = min(kIds, n_here - c0);
-        cblk = blk + c0;
-        const int f_raw = block_tables[(size_t)b * mbps + min(cblk + lane, nblk - 1)];
-        const bool ok = lane < cn && f_raw >= 0 && (long long)f_raw < NB;
-        live_mask = __ballot(ok);
-        vfid = ok ? f_raw : 0;
-        vstride = ok ? 1 : 0;
-        const int nsteps = (cn + F - 1) / F;
-        load_step(kA, vA, 0);
-        load_step(kB, vB, 1);
-        for (int s = 0; s < nsteps; s += 2) {
-          compute_step(kA, vA, s);
-          load_step(kA, vA, s + 2);
-          compute_step(kB, vB, s + 1);
-          load_step(kB, vB, s + 3);
-        }
-      }
-
-      const float lrow = wave_sum_over_j(lsum);
-      if (n < G) {
-        if (complete) {
-          const float inv = v_scale / lrow;
-          const size_t o = ((size_t)b * Hq + (size_t)g * G + n) * D + 4 * j;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            if constexpr (KIND == KF32) {
-              *(f32x4*)((float*)out + o + 16 * c) = acc[c] * inv;
-            } else {
-              u32x2 pk;
-              pk[0] = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
-              pk[1] = pack_bf16x2(acc[c][2] * inv, acc[c][3] * inv);
-              *(u32x2*)((__bf16*)out + o + 16 * c) = pk;
-            }
-          }
-        } else {
-          const size_t row = ((size_t)w * 2 + (s0 > a ? 1 : 0)) * 16 + n;
-#pragma unroll
-          for (int c = 0; c < NC; ++c) *(f32x4*)(ws_o + row * D + 16 * c + 4 * j) = acc[c];
-          if (j == 0) {
-            ws_ml[2 * row] = m;
-            ws_ml[2 * row + 1] = lrow;
-          }
-        }
-      }
-    }
-    x += units > 0 ? units : 0;
-    u = 0;
-    if (++g == Hkv) {
-      g = 0;
-      ++b;
     }
   }
+  // the loads of the last two steps (past the range) land before the wavefront ends
 }
 
 // Merge the partials of the runs cut by wavefront range boundaries:
