@@ -130,22 +130,35 @@ __device__ __forceinline__ void prefill_tile(
   // Wavefront w copies blocks w, w + 8, ... straight from global memory into the stage's LDS
   // buffer with LDS-DMA loads (lane l's 16 bytes land at the block's base + 16 l): no register or
   // LDS store of the wavefront carries them, and the copy of a later stage runs while this one
-  // is computed.  Frames past kend, invalid ids and stages past the last copy the first 16 bytes
-  // of the K cache instead (never used), so every stage issues the same loads and the wait
-  // counts below hold.
+  // is computed.
   constexpr int NBLK = STAGE / 1024;
   constexpr int BPW = (NBLK + kPWaves - 1) / kPWaves;  // blocks per wavefront and stage
   static_assert(NBLK % kPWaves == 0 || NBLK < kPWaves, "stage blocks must split over waves");
+  static_assert(64 % SF == 0, "a stage's frames lie in one window of 64 block ids");
+  // Block ids come in windows of 64 frames, one per lane, fetched one window ahead with a single
+  // vector load: lane l of window wi holds the id of frame kbeg / BS + 64 wi + l, or -1 if that
+  // frame lies past the range end or the id is outside the pool.  Stages read their ids with
+  // readlane, so issuing a stage's copies never waits for memory.
+  const int F0 = kbeg / BS;
+  auto load_window = [&](int wi) {
+    const int fi = F0 + 64 * wi + lane;
+    int f = -1;
+    if (fi * BS < kend) f = block_tables[trow + fi];
+    return (f >= 0 && (long long)f < NB) ? f : -1;
+  };
+  int win = 0;                    // window held in ids_cur
+  int ids_cur = load_window(0);
+  int ids_nxt = load_window(1);
   auto dma = [&](char* buf, int st) {
-    const int key0 = kbeg + SK * st;
+    const int wi = (st * SF) >> 6;
+    if (wi != win) {  // wavefront-uniform; stages are copied in order
+      win = wi;
+      ids_cur = ids_nxt;
+      ids_nxt = load_window(wi + 1);
+    }
     int fid[SF];
 #pragma unroll
-    for (int fl = 0; fl < SF; ++fl) {
-      const int fi = key0 / BS + fl;
-      int f = -1;
-      if (st < nst && fi * BS < kend) f = block_tables[trow + fi];
-      fid[fl] = uniform((f >= 0 && (long long)f < NB) ? f : -1);
-    }
+    for (int fl = 0; fl < SF; ++fl) fid[fl] = __builtin_amdgcn_readlane(ids_cur, (st * SF + fl) & 63);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
       const int blk = w + k * kPWaves;
@@ -155,9 +168,11 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
       for (int z = 1; z < SF; ++z)
         if (fl == z) f = fid[z];
+      // frames past the range and invalid ids copy 16 bytes of frame 0 into every lane's slot
+      // (never used): every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      const u32x4* src = f >= 0 ? (const u32x4*)(base + ((size_t)f * Hkv + g) * TILE + r * 1024) + lane
-                                : (const u32x4*)k_cache;
+      const size_t fo = f >= 0 ? (size_t)f : 0;
+      const u32x4* src = (const u32x4*)(base + (fo * Hkv + g) * TILE + r * 1024) + (f >= 0 ? lane : 0);
       lds_dma16(src, buf + blk * 1024);
     }
   };
