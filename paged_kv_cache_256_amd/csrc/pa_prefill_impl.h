@@ -64,7 +64,7 @@ __device__ __forceinline__ void prefill_tile(
 
   static_assert(STAGE == prefill_stage_bytes<KIND, D, BS>(), "stage size");
 
-  const int w = uniform(threadIdx.x >> 6);
+  const int w = uniform(threadIdx.x >> 6) & (kPWaves - 1);  // (the mask tells the compiler w < 8)
   const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
 
   const int r0 = qsl[c];
@@ -136,44 +136,58 @@ __device__ __forceinline__ void prefill_tile(
   static_assert(NBLK % kPWaves == 0 || NBLK < kPWaves, "stage blocks must split over waves");
   static_assert(64 % SF == 0, "a stage's frames lie in one window of 64 block ids");
   // Block ids come in windows of 64 frames, one per lane, fetched one window ahead with a single
-  // vector load: lane l of window wi holds the id of frame kbeg / BS + 64 wi + l, or -1 if that
-  // frame lies past the range end or the id is outside the pool.  Stages read their ids with
-  // readlane, so issuing a stage's copies never waits for memory.
+  // vector load: lane l of window wi loads the table entry of frame kbeg / BS + 64 wi + l (the
+  // index clamped to the range's last frame, so the load needs no branch).  When a window
+  // becomes current, its lanes turn their entries into tile indices f Hkv + g, or -1 for frames
+  // past the range and ids outside the pool, in vector code once for its 64 frames; a stage then
+  // only reads its frames' indices with readlane.  The one wait on a window's load lands a window
+  // after the load was issued, and the next window is requested after the copies of the stage
+  // that starts a window.  (The scalar unit is shared by the CU's eight wavefronts: the per-stage
+  // copy issue is kept to a few scalar instructions per block.)
   const int F0 = kbeg / BS;
-  auto load_window = [&](int wi) {
+  const int Flast = (kend - 1) / BS;  // last frame of the range
+  const int nb32 = NB < 0x7fffffffLL ? (int)NB : 0x7fffffff;  // every valid id is below it
+  auto load_window = [&](int wi) { return block_tables[trow + min(F0 + 64 * wi + lane, Flast)]; };
+  auto tiles_of = [&](int raw, int wi) {
     const int fi = F0 + 64 * wi + lane;
-    int f = -1;
-    if (fi * BS < kend) f = block_tables[trow + fi];
-    return (f >= 0 && (long long)f < NB) ? f : -1;
+    return (fi * BS < kend && raw >= 0 && raw < nb32) ? raw * Hkv + g : -1;
   };
-  int win = 0;                    // window held in ids_cur
-  int ids_cur = load_window(0);
-  int ids_nxt = load_window(1);
+  int win = 0;  // window held in tix_cur
+  int tix_cur = tiles_of(load_window(0), 0);
+  int raw_nxt = load_window(1);
   auto dma = [&](char* buf, int st) {
     const int wi = (st * SF) >> 6;
-    if (wi != win) {  // wavefront-uniform; stages are copied in order
+    const bool next = wi != win;  // wavefront-uniform; stages are copied in order
+    if (next) {
+      // (the empty statement keeps this a branch: as a select, the conversion would read
+      // raw_nxt, a load the compiler cannot see completed, at every stage and wait there)
+      asm volatile("");
+      tix_cur = tiles_of(raw_nxt, wi);
       win = wi;
-      ids_cur = ids_nxt;
-      ids_nxt = load_window(wi + 1);
     }
-    int fid[SF];
+    int tix[SF];
 #pragma unroll
-    for (int fl = 0; fl < SF; ++fl) fid[fl] = __builtin_amdgcn_readlane(ids_cur, (st * SF + fl) & 63);
+    for (int fl = 0; fl < SF; ++fl) tix[fl] = __builtin_amdgcn_readlane(tix_cur, (st * SF + fl) & 63);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
       const int blk = w + k * kPWaves;
       if (NBLK < kPWaves && blk >= NBLK) break;  // wavefront-uniform
       const int fl = blk / (2 * NL), kind = (blk / NL) & 1, r = blk % NL;
-      int f = fid[0];
+      int t = tix[0];
 #pragma unroll
       for (int z = 1; z < SF; ++z)
-        if (fl == z) f = fid[z];
-      // frames past the range and invalid ids copy 16 bytes of frame 0 into every lane's slot
+        if (fl == z) t = tix[z];
+      // frames past the range and invalid ids copy 16 bytes of tile 0 into every lane's slot
       // (never used): every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      const size_t fo = f >= 0 ? (size_t)f : 0;
-      const u32x4* src = (const u32x4*)(base + (fo * Hkv + g) * TILE + r * 1024) + (f >= 0 ? lane : 0);
+      const u32x4* src = (const u32x4*)(base + (size_t)(uint32_t)max(t, 0) * TILE + r * 1024) +
+                         (t >= 0 ? lane : 0);
       lds_dma16(src, buf + blk * 1024);
+    }
+    if (next) {
+      // the window after the new one, requested after this stage's copies
+      __builtin_amdgcn_sched_barrier(0);
+      raw_nxt = load_window(wi + 1);
     }
   };
   // Wait until this wavefront's copies of every stage but the newest have landed in LDS, then
