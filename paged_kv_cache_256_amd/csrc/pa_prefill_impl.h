@@ -201,10 +201,10 @@ __device__ __forceinline__ void prefill_tile(
     }
   };
 
-  // Scores of stage st (K from LDS buffer st % 3).
-  auto qk = [&](const char* sb, f32x4 (&s)[NT][NG]) {
+  // Scores of frames [f_lo, f_hi) of a stage (K from its LDS buffer).
+  auto qk = [&](const char* sb, f32x4 (&s)[NT][NG], int f_lo, int f_hi) {
 #pragma unroll
-    for (int fl = 0; fl < SF; ++fl) {
+    for (int fl = f_lo; fl < f_hi; ++fl) {
       u32x4 kt[NL];
 #pragma unroll
       for (int r = 0; r < NL; ++r)
@@ -222,9 +222,9 @@ __device__ __forceinline__ void prefill_tile(
     }
   };
 
-  // Softmax and P.V of stage st (V from LDS buffer st % 3).  `overlap` runs between the
-  // shift update and the exponentials, in the same basic block as the exponentials and the
-  // P.V products, so that the score MFMAs it issues for the next stage interleave with them.
+  // Softmax and P.V of stage st (V from its LDS buffer).  `overlap(pp)` issues the score MFMAs
+  // of part pp of the next stage next to the exponentials and P.V products of pair pp, so that
+  // the matrix cores and the vector ALUs work side by side.
   auto finish = [&](int st, const char* sb, f32x4 (&s)[NT][NG], auto&& overlap) {
     const int key0 = kbeg + SK * st;
     // Online softmax per query row with a lazily moved shift: m[t] only moves (and the
@@ -273,27 +273,34 @@ __device__ __forceinline__ void prefill_tile(
         for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
       }
     }
-    overlap();
-    typename Ops::PFrag pf[NT][NG];
+    // Per pair of 16-key groups: the score products of the next stage's frames that the pair's
+    // index selects (`overlap`), the pair's exponentials, and its P.V products.  The compiler
+    // interleaves the score products with the exponentials (and the P.V products of a pair with
+    // the next pair's work); splitting the stage into pairs keeps the registers in flight to
+    // about one pair's worth (the whole stage as one block spills).
+    const bool tail = key0 + SK > kend;
+    float nm[NT];  // the exponentials' shift
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const float nm = m[t] == -INFINITY ? 0.f : -m[t];
-#pragma unroll
-      for (int gi = 0; gi < NG; ++gi) {
-        f32x4 p;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          // a masked score is -inf and qk_abs > 0: its probability is exactly 0
-          p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][gi][ii], qk_abs, nm));
-        }
-        pf[t][gi] = Ops::pfrag(p, lsum[t]);
-      }
-    }
+    for (int t = 0; t < NT; ++t) nm[t] = m[t] == -INFINITY ? 0.f : -m[t];
     // P * V over pairs of 16-key groups (one 16x16x32 product each); with 16-key frames the two
     // groups are two frames, with 32-key frames the two halves of one
-    const bool tail = key0 + SK > kend;
 #pragma unroll
     for (int pp = 0; pp < NG / 2; ++pp) {
+      overlap(pp);
+      typename Ops::PFrag pf[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 p;
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            // a masked score is -inf and qk_abs > 0: its probability is exactly 0
+            p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * pp + h][ii], qk_abs, nm[t]));
+          }
+          pf[t][h] = Ops::pfrag(p, lsum[t]);
+        }
+      }
       constexpr int FPP = KG == 1 ? 2 : 1;  // frames per pair
       u32x4 vt[FPP][NL];
 #pragma unroll
@@ -317,7 +324,7 @@ __device__ __forceinline__ void prefill_tile(
         const auto vb = Ops::vop(vt[1 / KG], 1 % KG, cc);
 #pragma unroll
         for (int t = 0; t < NT; ++t)
-          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][2 * pp], pf[t][2 * pp + 1]);
+          acc[t][cc] = Ops::pv2(acc[t][cc], va, vb, pf[t][0], pf[t][1]);
       }
     }
   };
@@ -331,7 +338,7 @@ __device__ __forceinline__ void prefill_tile(
   dma(ring2, 2);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   f32x4 sa[NT][NG], sz[NT][NG];
-  qk(ring0, sa);
+  qk(ring0, sa, 0, SF);
   // one stage: copy stage st + 3 into the buffer stage st - 1 used, finish stage st (its scores
   // in s_cur) while the scores of stage st + 1 go into s_nxt, meet
   auto stage = [&](int st, const char* cur, const char* nxt, char* free_buf, f32x4 (&s_cur)[NT][NG],
@@ -339,7 +346,10 @@ __device__ __forceinline__ void prefill_tile(
     dma(free_buf, st + 3);
     // (past the last stage the next-stage scores read a buffer already written and are never
     // used: issuing them unconditionally keeps them in the exponentials' block)
-    finish(st, cur, s_cur, [&] { qk(nxt, s_nxt); });
+    // the next stage's frames scored while pair pp of this stage is finished
+    constexpr int FQ = 2 * SF / NG;
+    auto next_scores = [&](int pp) { qk(nxt, s_nxt, pp * FQ, (pp + 1) * FQ); };
+    finish(st, cur, s_cur, next_scores);
     sync_stage();
   };
   for (int st = 0; st < nst; st += 4) {
