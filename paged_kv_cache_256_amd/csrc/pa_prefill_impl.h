@@ -23,11 +23,32 @@ struct PQ {
 // One LDS-DMA copy (global_load_lds_dwordx4): each lane's 16 bytes at src land at lds + 16 lane.
 // Issued as assembly so that the compiler does not make unrelated LDS reads wait for it (the
 // pipeline below waits for the copies itself); the kernels that use it leave M0 to it.
-__device__ inline void lds_dma16(const void* src, char* lds) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds);
+__device__ inline void lds_dma16(const void* src, uint32_t lds_addr) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
                : "memory");
+}
+
+// The 32-bit LDS address of a pointer into a __shared__ buffer.
+__device__ inline uint32_t lds_address(const char* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// P^T fragment of four probabilities for the prefill tile.  bf16 / fp8 kinds: rounded to bf16
+// for the matrix core, and the row sum taken over the fp32 values before rounding (four
+// additions, no unpacking); the normalisation then differs from the rounded weights by a
+// relative error of about 2^-9 / sqrt(keys), far below the bf16 output's own rounding.
+template <int KIND, class Ops>
+__device__ inline typename Ops::PFrag prefill_pfrag(f32x4 p, float& lsum) {
+  if constexpr (KIND == KF32) {
+    return Ops::pfrag(p, lsum);
+  } else {
+    u32x2 pp;
+    pp[0] = pack_bf16x2(p[0], p[1]);
+    pp[1] = pack_bf16x2(p[2], p[3]);
+    lsum += (p[0] + p[1]) + (p[2] + p[3]);
+    return pp;
+  }
 }
 
 // Keys per pipeline stage: 64 (32 for f32, whose tiles are twice as large: a ring of four 64-key
@@ -146,6 +167,7 @@ __device__ __forceinline__ void prefill_tile(
   // copy issue is kept to a few scalar instructions per block.)
   const int F0 = kbeg / BS;
   const int Flast = (kend - 1) / BS;  // last frame of the range
+  const int lane16 = lane * 16;       // byte offset of a lane's 16 bytes in a 1 KiB block
   const int nb32 = NB < 0x7fffffffLL ? (int)NB : 0x7fffffff;  // every valid id is below it
   auto load_window = [&](int wi) { return block_tables[trow + min(F0 + 64 * wi + lane, Flast)]; };
   auto tiles_of = [&](int raw, int wi) {
@@ -168,6 +190,7 @@ __device__ __forceinline__ void prefill_tile(
     int tix[SF];
 #pragma unroll
     for (int fl = 0; fl < SF; ++fl) tix[fl] = __builtin_amdgcn_readlane(tix_cur, (st * SF + fl) & 63);
+    const uint32_t buf_lds = lds_address(buf);
 #pragma unroll
     for (int k = 0; k < BPW; ++k) {
       const int blk = w + k * kPWaves;
@@ -180,9 +203,8 @@ __device__ __forceinline__ void prefill_tile(
       // frames past the range and invalid ids copy 16 bytes of tile 0 into every lane's slot
       // (never used): every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      const u32x4* src = (const u32x4*)(base + (size_t)(uint32_t)max(t, 0) * TILE + r * 1024) +
-                         (t >= 0 ? lane : 0);
-      lds_dma16(src, buf + blk * 1024);
+      const char* src = base + (size_t)(uint32_t)max(t, 0) * TILE + r * 1024 + (t >= 0 ? lane16 : 0);
+      lds_dma16(src, buf_lds + blk * 1024);
     }
     if (next) {
       // the window after the new one, requested after this stage's copies
@@ -298,7 +320,7 @@ __device__ __forceinline__ void prefill_tile(
             // a masked score is -inf and qk_abs > 0: its probability is exactly 0
             p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][2 * pp + h][ii], qk_abs, nm[t]));
           }
-          pf[t][h] = Ops::pfrag(p, lsum[t]);
+          pf[t][h] = prefill_pfrag<KIND, Ops>(p, lsum[t]);
         }
       }
       constexpr int FPP = KG == 1 ? 2 : 1;  // frames per pair
