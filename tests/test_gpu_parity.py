@@ -110,6 +110,35 @@ def test_prefill_chunk_small(kv, D, bs, G, chunks, dec):
         _check_decode(g, o)
 
 
+# Context ranges longer than one 64-frame window of block ids: enough query tiles (a 512-row chunk
+# over 8 KV heads) that the context splits only a few ways, so each range crosses two window
+# switches and ends in a ragged window -- with 16-token bf16 frames (4 ranges of 2,304 keys, 144
+# frames) and 32-token fp8 frames (2 ranges of 6,016 keys, 188 frames).
+LONG_RANGE_CASES = [
+    ("bf16", 16, 4, 9000),
+    ("fp8", 32, 8, 12000),
+]
+
+
+@pytest.mark.parametrize("kv,bs,G,L", LONG_RANGE_CASES,
+                         ids=[f"{c[0]}-bs{c[1]}-G{c[2]}-L{c[3]}" for c in LONG_RANGE_CASES])
+def test_prefill_ranges_spanning_several_id_windows(kv, bs, G, L):
+    Hkv = 8
+    _say(f"long-range prefill kv={kv} bs={bs} G={G} chunk 512 at context {L}")
+    c = workloads.chunk_case("long-range", 500 + bs + G, Hq=G * Hkv, Hkv=Hkv, D=128, bs=bs,
+                             chunks=[(512, L)], decode_lens=[], kv_dtype=kv, std=0.7071)
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_caches(g, o)
+    rng = np.random.default_rng(17)
+    rows = sorted(set(rng.choice(512, size=40, replace=False).tolist()) | {0, 31, 32, 255, 256, 511})
+    got = out_f64(g.chunk_out)[rows]
+    assert np.isfinite(got).all()
+    err = np.abs(got - o.prefill(rows)[rows]).max()
+    _say(f"  max abs err {err:.2e} over {len(rows)} rows")
+    assert err <= tolerance(c), f"prefill max abs err {err:.3e}"
+
+
 def test_copy_blocks_bit_exact_and_shared_equals_private():
     c = workloads.cases.fork_case("fork", 31, prompts=3, branches=4, prompt_len=64, tail_lo=3,
                                   tail_hi=70, Hq=16, Hkv=2, D=128, bs=32, kv_dtype="fp8")
