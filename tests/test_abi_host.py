@@ -74,6 +74,20 @@ def test_package_import_fails_loudly_without_the_library(tmp_path):
     assert "ImportError" in r.stderr and "no fallback" in r.stderr
 
 
+def test_builder_loads_on_a_tree_without_the_library(tmp_path):
+    """build() has to work where libpa.so does not exist yet: the builder module is loaded by
+    path, since importing the package requires the library."""
+    shutil.copytree(os.path.join(ROOT, "paged_kv_cache_256_amd"), tmp_path / "paged_kv_cache_256_amd",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copy(os.path.join(ROOT, "__graft_entry__.py"), tmp_path)
+    code = ("import __graft_entry__ as g, sys; m = g._load_builder(); "
+            "assert callable(m.build) and 'pa_decode.hip' in m.SOURCES; "
+            "assert 'paged_kv_cache_256_amd' not in sys.modules; print('ok')")
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                       env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
 # ----------------------------------------------------------------------------- pa_decode
 
 
