@@ -44,6 +44,8 @@ using namespace dec;
 
 namespace {
 
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+
 // The same plan for any batch size, in one workgroup: thread t owns the contiguous sequences
 // [t*per, (t+1)*per); a block-wide scan of the per-thread unit counts gives every thread its
 // offset; each wavefront start is then located by a binary search over the 1024 per-thread
@@ -111,8 +113,14 @@ __global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
     const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
     long long NB, int cap, float qk_scale, float v_scale) {
+  // Workgroups reach the 8 XCDs round-robin by id.  XCD k (workgroups k, k + 8, ...) takes the
+  // k-th eighth of the ranges, so that runs next to each other in the batch -- branches that share
+  // frames -- stream through the same L2.
+  const int nwg = gridDim.x;
+  const int r = nwg % kXcds == 0 ? (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds
+                                 : blockIdx.x;
   decode_stream_wave<KIND, D, BS, F, NT>(
-      blockIdx.x * kWaves + uniform(threadIdx.x >> 6), gridDim.x * kWaves, out, q, k_cache,
+      r * kWaves + uniform(threadIdx.x >> 6), gridDim.x * kWaves, out, q, k_cache,
       v_cache, block_tables, context_lens, plan, inline_plan, ws_ml, ws_o, B, mbps, Hq, Hkv, G,
       NB, cap, qk_scale, v_scale);
 }
