@@ -102,8 +102,12 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void mixed_kernel(MixedArgs a) {
     }
     return;
   }
+  // decode workgroups: XCD k takes the k-th eighth of the decode ranges (as in pa_decode), when
+  // the prefill and decode workgroup counts keep the round-robin aligned
+  const int nd = (int)gridDim.x - a.P, rd = wg - a.P;
+  const int r = (a.P % kXcds == 0 && nd % kXcds == 0) ? (rd % kXcds) * (nd / kXcds) + rd / kXcds : rd;
   decode_stream_wave<KIND, D, BS, F, NTL>(
-      (wg - a.P) * kPWaves + uniform(threadIdx.x >> 6), ((int)gridDim.x - a.P) * kPWaves, a.out,
+      r * kPWaves + uniform(threadIdx.x >> 6), nd * kPWaves, a.out,
       a.q, a.k_cache, a.v_cache, a.block_tables, a.context_lens, a.plan, a.inline_plan, a.d_ml,
       a.d_o, a.B, a.mbps, a.Hq, a.Hkv, a.G, a.NB, a.dcap, a.qk_scale, a.v_scale);
 }

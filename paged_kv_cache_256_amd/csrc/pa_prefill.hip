@@ -29,17 +29,35 @@ using namespace pre;
 
 namespace {
 
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+
 template <int KIND, int D, int BS, int NT>
 __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int mbps, int Hq, int Hkv, int G,
-    long long NB, long long total_q, long long row_base, int nsplit, int KS, int max_ctx,
-    float qk_scale, float v_scale) {
+    long long NB, long long total_q, long long row_base, int nsplit, int nq, int nz, int KS,
+    int max_ctx, float qk_scale, float v_scale) {
   constexpr int S = prefill_stage_bytes<KIND, D, BS>();
   __shared__ __attribute__((aligned(1024))) char ring0[S], ring1[S], ring2[S], ring3[S];
-  prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, blockIdx.x, blockIdx.y, blockIdx.z / Hkv, blockIdx.z % Hkv,
+  // One workgroup per (key range x, query tile y, chunk and kv head z).  Workgroups reach the
+  // 8 XCDs round-robin by id; when the (x, z) groups -- tiles that read the same keys -- come in
+  // multiples of 8, every tile of a group is dealt to one XCD, so its keys are read into one L2.
+  const int id = blockIdx.x, groups = nsplit * nz;
+  int x, y, z;
+  if (groups % kXcds == 0) {
+    const int k = id % kXcds, slot = id / kXcds;
+    const int grp = k + kXcds * (slot / nq);
+    y = slot % nq;
+    x = grp % nsplit;
+    z = grp / nsplit;
+  } else {
+    x = id % nsplit;
+    y = (id / nsplit) % nq;
+    z = id / (nsplit * nq);
+  }
+  prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, x, y, z / Hkv, z % Hkv,
                                 row_base, out, q, k_cache, v_cache, block_tables, qsl, context_lens,
                                 ws_ml, ws_o, mbps, Hq, Hkv, G, NB, total_q, nsplit, KS, max_ctx,
                                 qk_scale, v_scale);
@@ -67,12 +85,14 @@ hipError_t launch_prefill_typed(const PrefillParams& p, hipStream_t stream) {
   float* ws_o = ws_ml ? ws_ml + partial_ml_floats(rows * p.Hq, sp.nsplit) : nullptr;
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
-  dim3 grid(sp.nsplit, (p.max_chunk_len + TQ - 1) / TQ, p.num_chunks * p.Hkv);
-  hipLaunchKernelGGL((prefill_chunk_kernel<KIND, D, BS, NT>), grid, dim3(kPWaves * 64), 0,
+  const int nq = (p.max_chunk_len + TQ - 1) / TQ, nz = p.num_chunks * p.Hkv;
+  const long long nwg = (long long)sp.nsplit * nq * nz;
+  if (nwg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((prefill_chunk_kernel<KIND, D, BS, NT>), dim3((unsigned)nwg), dim3(kPWaves * 64), 0,
                      stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
                      p.block_tables, p.query_start_loc, p.context_lens, ws_ml, ws_o,
                      p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB,
-                     (long long)p.total_q, (long long)p.row_base, sp.nsplit, sp.KS,
+                     (long long)p.total_q, (long long)p.row_base, sp.nsplit, nq, nz, sp.KS,
                      p.max_context_len, qk_scale, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sp.nsplit <= 1) return e;
