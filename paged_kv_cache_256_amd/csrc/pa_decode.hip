@@ -28,7 +28,11 @@
 // lane) and are broadcast with readlane; each step gathers F frames' K and V tiles straight into
 // registers (the tile layout puts every lane's matrix-core fragment in one 16-byte load, so a
 // tile is NL fully contiguous 1 KiB loads), double-buffered so that one step is in flight while
-// the other is computed.  Tiles are read with non-temporal loads: each is used once.  The G
+// the other is computed.  The pipeline does not drain between chunks of 64 frames or between
+// runs: the next chunk's ids and query are fetched during the current chunk, whose last two
+// load steps already gather the next chunk's first two.  Tiles are read with non-temporal loads:
+// each is used once (unless the caller flags frames shared between sequences).  The ranges are
+// dealt to the XCDs in contiguous eighths, so neighbouring runs share an L2.  The G
 // query heads of the group are the 16 columns of a 16x16 MFMA (GQA: the group shares every K/V
 // fragment; unused columns hold zero queries): S^T = K Q^T, an online softmax in the log2 domain
 // with the running max reduced across the 4 lanes holding a row, O^T += V^T P^T.  fp8 tiles are
