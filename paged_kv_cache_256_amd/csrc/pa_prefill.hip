@@ -13,10 +13,14 @@
 //    each wavefront copies its share of a later stage straight from global memory into LDS with
 //    LDS-DMA loads while the wavefronts compute, and every wavefront then reads the same tile
 //    from LDS, so one fetch from L2/HBM serves 8 x NT x 16 query rows.  One meeting point per
-//    stage; the copies of the next two stages stay in flight across it.
+//    stage; the copies of the next two stages stay in flight across it.  The block ids come in
+//    windows of 64 frames (one vector load, a window ahead) and are turned into tile indices once
+//    per window, so issuing a stage's copies costs a few scalar instructions per block and never
+//    waits for memory.
 //  * Online softmax per query row (causal mask on the diagonal stages), O^T += V^T P^T with
-//    16x16x32 products over pairs of 16-key groups; the score MFMAs of the next stage are issued
-//    inside the current stage's softmax.
+//    16x16x32 products over pairs of 16-key groups; each pair also issues its part of the next
+//    stage's score MFMAs, so the matrix cores work beside the exponentials.
+//  * Tiles that read the same key range are dealt to one XCD, so the range is read into one L2.
 //  * The context is split into KS-key ranges across workgroups so that a single chunk fills
 //    the GPU; rows covered by one range are written directly, the others as unnormalised
 //    partials merged by prefill_reduce_kernel (log-sum-exp rule).
