@@ -139,7 +139,9 @@ size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype 
  *                 aligned (hipMalloc'd memory is).  Nothing in it is read before this call
  *                 writes it; concurrent calls must not share one.
  * The batch's (sequence, kv head, frame) work is split into equal contiguous ranges over a
- * fixed set of persistent wavefronts; a sequence cut by a range boundary is merged from
+ * set of persistent wavefronts (three per compute unit, fewer when the host-known bound
+ * B Hkv ceil(max_context_len / block_size) leaves too little work for them, so the launch
+ * depends on B, Hkv, block_size and max_context_len only); a sequence cut by a range boundary is merged from
  * partial results by a second (reduce) kernel, exactly up to fp32 rounding ("CUDA Shared
  * Memory Optimization": a final normalised reduction).  The merge order is fixed, so equal
  * inputs give equal output bits.

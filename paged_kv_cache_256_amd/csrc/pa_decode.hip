@@ -137,16 +137,30 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
                               v_scale);
 }
 
+// Wavefronts of a launch: the full stream (3 per CU) unless the batch holds too few units for it.
+// The host knows an upper bound of the units, B Hkv (ceil(cap / BS) + kRestart); each wavefront
+// gets at least kMinUnitsPerWave of it, so a small batch is not cut into one-frame pieces that
+// each pay the whole latency chain (plan, ids, tiles, partial, merge).
+constexpr long long kMinUnitsPerWave = 32;
+
+inline int launch_waves(int B, int Hkv, int cap, int BS) {
+  const long long units = (long long)B * Hkv * ((cap + BS - 1) / BS + kRestart);
+  const long long want = (units + kMinUnitsPerWave - 1) / kMinUnitsPerWave;
+  const long long w = (want + kWaves - 1) / kWaves * kWaves;
+  const int full = stream_waves();
+  return w >= full ? full : (int)(w > kWaves ? w : kWaves);
+}
+
 template <int KIND, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   constexpr int F = step_frames<KIND, D, BS>();
-  const Layout l = layout(D, stream_waves());
+  const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
+                                                                 : p.max_blocks_per_seq * BS;
+  const Layout l = layout(D, launch_waves(p.B, p.Hkv, cap, BS));  // within the workspace's size
   int32_t* plan = (int32_t*)p.workspace;
   float* ws_ml = (float*)((char*)p.workspace + l.plan_bytes);
   float* ws_o = (float*)((char*)p.workspace + l.plan_bytes + l.ml_bytes);
   const int G = p.Hq / p.Hkv;
-  const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
-                                                                 : p.max_blocks_per_seq * BS;
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
   const bool inline_plan = p.B <= kInlinePlanMax;
