@@ -91,7 +91,8 @@ const char* pa_build_info(void);
  * Defined by the block-table mapping (codebumble.net, "The Block Table Mapping
  * Subsystem"): token i goes to frame slot_mapping[i] / block_size at offset
  * slot_mapping[i] % block_size, for every KV head.
- *   k, v          [T, Hkv, D] rows in src_dtype (f32 or bf16), contiguous.
+ *   k, v          [T, Hkv, D] rows in src_dtype (f32 or bf16), contiguous, 16-byte aligned
+ *                 (as are the caches; PA_EINVAL otherwise).
  *   k_cache, v_cache  caches in kv_dtype, layout above, written in place.
  *   slot_mapping  int64 [T]; a negative slot skips the token (padding).  Two tokens must
  *                 not name the same slot in one call (the later write is unspecified).

@@ -134,6 +134,8 @@ int pa_reshape_and_cache(const void* k, const void* v, void* k_cache, void* v_ca
   if (T > 0x7fffffff) return fail(PA_ENOTSUP, "T %lld too large for one call", (long long)T);
   if (T == 0) return ok();
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return fail(PA_EINVAL, "null pointer argument");
+  if (((uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache) & 15)
+    return fail(PA_EINVAL, "k, v and the caches must be 16-byte aligned");
   return hip_status(pa::launch_reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, T, NB, Hkv, D,
                                                  block_size, src_dtype, kv_dtype, k_scale, v_scale,
                                                  (hipStream_t)stream),

@@ -31,14 +31,31 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   constexpr int TILE = BS * D * EB;
   constexpr int EPC = 16 / EB;  // elements per 16-byte piece
   static_assert((D / 4) % EPC == 0, "a piece must not cross a fragment");
+  constexpr int SB = SRC == KF32 ? 4 : 2;  // bytes of a source element
+  typedef uint32_t SrcPiece __attribute__((ext_vector_type(EPC * SB / 4)));
   const long long i = blockIdx.x;
+  // The source rows do not depend on the slot: the first piece of each thread is loaded before
+  // the slot is known, so the two loads overlap instead of forming a chain.
+  const int npc = Hkv * (D / EPC);
+  SrcPiece k0 = {}, v0 = {};
+  if ((int)threadIdx.x < npc) {
+    const size_t src0 = ((size_t)i * Hkv * D + (size_t)threadIdx.x * EPC) * SB;
+    k0 = *(const SrcPiece*)((const char*)k + src0);
+    v0 = *(const SrcPiece*)((const char*)v + src0);
+  }
   const long long s = slots[i];
   if (s < 0 || s >= NB * BS) return;
   const long long f = s / BS;
   const int o = (int)(s % BS);
-  for (int pc = threadIdx.x; pc < Hkv * (D / EPC); pc += blockDim.x) {
+  for (int pc = threadIdx.x; pc < npc; pc += blockDim.x) {
     const int g = pc / (D / EPC), d0 = (pc % (D / EPC)) * EPC;
     const size_t src = ((size_t)i * Hkv + g) * D + d0;
+    if (pc != (int)threadIdx.x) {
+      k0 = *(const SrcPiece*)((const char*)k + src * SB);
+      v0 = *(const SrcPiece*)((const char*)v + src * SB);
+    }
+    const char* ks = (const char*)&k0;
+    const char* vs = (const char*)&v0;
     const size_t tile = ((size_t)f * Hkv + g) * TILE;
     u32x4 kp;
     uint8_t* kb = (uint8_t*)&kp;
@@ -47,19 +64,19 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
     for (int e = 0; e < EPC; ++e) {
       char* vdst = vd + v_tile_byte(o, d0 + e, D, EB);
       if constexpr (KV == KF32) {
-        ((uint32_t*)kb)[e] = ((const uint32_t*)k)[src + e];
-        *(uint32_t*)vdst = ((const uint32_t*)v)[src + e];
+        ((uint32_t*)kb)[e] = ((const uint32_t*)ks)[e];
+        *(uint32_t*)vdst = ((const uint32_t*)vs)[e];
       } else if constexpr (KV == KBF16) {
-        ((uint16_t*)kb)[e] = ((const uint16_t*)k)[src + e];
-        *(uint16_t*)vdst = ((const uint16_t*)v)[src + e];
+        ((uint16_t*)kb)[e] = ((const uint16_t*)ks)[e];
+        *(uint16_t*)vdst = ((const uint16_t*)vs)[e];
       } else {
         float xk, xv;
         if constexpr (SRC == KF32) {
-          xk = ((const float*)k)[src + e];
-          xv = ((const float*)v)[src + e];
+          xk = ((const float*)ks)[e];
+          xv = ((const float*)vs)[e];
         } else {
-          xk = __uint_as_float((uint32_t)((const uint16_t*)k)[src + e] << 16);
-          xv = __uint_as_float((uint32_t)((const uint16_t*)v)[src + e] << 16);
+          xk = __uint_as_float((uint32_t)((const uint16_t*)ks)[e] << 16);
+          xv = __uint_as_float((uint32_t)((const uint16_t*)vs)[e] << 16);
         }
         kb[e] = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xk, k_scale));
         *(uint8_t*)vdst = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xv, v_scale));

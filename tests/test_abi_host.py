@@ -205,6 +205,8 @@ def test_reshape_and_cache_rejects_bad_arguments():
     assert f(*args(T=1 << 31)) == ENOTSUP
     assert f(*args(T=0, k=NULL, s=NULL)) == OK
     assert f(*args(D=32)) == ENOTSUP
+    # the source rows are read with 16-byte loads
+    assert f(*args(k=ctypes.c_void_p(0x1002))) == EINVAL and "16-byte aligned" in err()
 
 
 def test_copy_blocks_rejects_bad_arguments():
