@@ -226,6 +226,11 @@ def main():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="run three plain device copies of this many MiB before the timed steps "
                          "(a known-size reference for hardware byte counters)")
+    ap.add_argument("--chunk-kv", default=None, choices=["bf16", "fp8"],
+                    help="config 5 only: the same mixed step with this KV cache dtype (fp8: "
+                         "per-tensor scales) -- the fp8 prefill-chunk variant")
+    ap.add_argument("--chunk-block-size", type=int, default=None, choices=[16, 32],
+                    help="config 5 only: the same mixed step with this block size")
     ap.add_argument("--block-manager", action="store_true",
                     help="time the host block manager (no GPU): prompts, decode steps with their "
                          "block-table export, and copy-on-write forks, for the 70B-shape batch")
@@ -245,7 +250,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    case = workloads.make(args.config)
+    if args.chunk_kv or args.chunk_block_size:
+        if args.config != 5:
+            print("bench.py: --chunk-kv / --chunk-block-size apply to --config 5 only",
+                  file=sys.stderr)
+            sys.exit(2)
+        case = workloads.config5_variant(kv_dtype=args.chunk_kv or "bf16",
+                                         bs=args.chunk_block_size or 16)
+    else:
+        case = workloads.make(args.config)
     log(f"[bench] generated config {args.config} ({case.name}) in {time.time() - t0:.1f}s")
     st = DeviceState(case, dev)
     torch.cuda.synchronize()

@@ -14,6 +14,7 @@ from .cases import (  # noqa: F401
     make,
     decode_case,
     chunk_case,
+    config5_variant,
     fork_case,
     mixed_batch,
     MixedBatch,

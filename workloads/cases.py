@@ -420,6 +420,17 @@ def _uniform_lens(lo: int, hi: int, n: int):
     return lambda rng: rng.integers(lo, hi + 1, size=n).astype(np.int64)
 
 
+def config5_variant(kv_dtype: str = "bf16", bs: int = 16, seed: int = 5) -> DecodeCase:
+    """Config 5's mixed step (a 512-token chunk at 16,384 tokens + 128 decodes, Llama-3-8B
+    shapes) with another KV dtype or block size: the fp8 / 32-token-block prefill variants."""
+    c = chunk_case(f"llama3-8b-mixed chunk512@16384 + 128 decodes {kv_dtype} bs{bs}", seed, Hq=32,
+                   Hkv=8, D=128, bs=bs, chunks=[(512, 16384)],
+                   decode_lens=_uniform_lens(256, 4096, 128), kv_dtype=kv_dtype,
+                   std=1.0 / math.sqrt(2.0))
+    c.meta["cfg"] = 5
+    return c
+
+
 def make(cfg: int, seed: int | None = None) -> DecodeCase:
     """The five named workloads at full size (seed defaults to the config number)."""
     seed = cfg if seed is None else seed
