@@ -84,7 +84,9 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void mixed_kernel(MixedArgs a) {
   constexpr int NT = tiles_per_wave(KIND);
   constexpr int F = step_frames<KIND, D, BS>();
   constexpr int S = prefill_stage_bytes<KIND, D, BS>();
+  constexpr int SW = prefill_widened_bytes<KIND, D, BS>();
   __shared__ __attribute__((aligned(1024))) char ring0[S], ring1[S], ring2[S], ring3[S];
+  __shared__ __attribute__((aligned(1024))) char wide0[SW], wide1[SW];
   const int wg = blockIdx.x;
   if (wg < a.P) {
     // tiles are ordered key range (x, chunk, kv head) first, query tile last; with P a multiple
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void mixed_kernel(MixedArgs a) {
     for (int t = rank; t < a.tiles; t += a.P) {
       const int grp = t / a.QT, qt = t - grp * a.QT;
       const int x = grp / ncg, cg = grp - x * ncg;
-      prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, x, qt, cg / a.Hkv, cg % a.Hkv, a.row_base, a.out,
+      prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, wide0, wide1, x, qt, cg / a.Hkv, cg % a.Hkv, a.row_base, a.out,
                                     a.q, a.k_cache, a.v_cache, a.tables_c, a.qsl_c, a.lens_c,
                                     a.p_ml, a.p_o, a.mbps, a.Hq, a.Hkv, a.G, a.NB, a.total_q,
                                     a.nsplit, a.KS, a.max_ctx, a.qk_scale, a.v_scale);

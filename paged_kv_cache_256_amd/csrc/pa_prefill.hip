@@ -44,7 +44,9 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     long long NB, long long total_q, long long row_base, int nsplit, int nq, int nz, int KS,
     int max_ctx, float qk_scale, float v_scale) {
   constexpr int S = prefill_stage_bytes<KIND, D, BS>();
+  constexpr int SW = prefill_widened_bytes<KIND, D, BS>();
   __shared__ __attribute__((aligned(1024))) char ring0[S], ring1[S], ring2[S], ring3[S];
+  __shared__ __attribute__((aligned(1024))) char wide0[SW], wide1[SW];
   // One workgroup per (key range x, query tile y, chunk and kv head z).  Workgroups reach the
   // 8 XCDs round-robin by id; when the (x, z) groups -- tiles that read the same keys -- come in
   // multiples of 8, every tile of a group is dealt to one XCD, so its keys are read into one L2.
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kPWaves * 64, 1) void prefill_chunk_kernel(
     y = (id / nsplit) % nq;
     z = id / (nsplit * nq);
   }
-  prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, x, y, z / Hkv, z % Hkv,
+  prefill_tile<KIND, D, BS, NT>(ring0, ring1, ring2, ring3, wide0, wide1, x, y, z / Hkv, z % Hkv,
                                 row_base, out, q, k_cache, v_cache, block_tables, qsl, context_lens,
                                 ws_ml, ws_o, mbps, Hq, Hkv, G, NB, total_q, nsplit, KS, max_ctx,
                                 qk_scale, v_scale);

@@ -62,25 +62,42 @@ constexpr int prefill_stage_bytes() {
   return (stage_keys(KIND) / BS) * 2 * KvOps<KIND, D, BS>::TILE;
 }
 
+// fp8 stages are widened once to bf16 in LDS (two buffers of this size): the bytes of one
+// widened stage, or a token size for the other kinds, which read their stages directly.
+template <int KIND, int D, int BS>
+constexpr int prefill_widened_bytes() {
+  return KIND == KFP8 ? prefill_stage_bytes<KBF16, D, BS>() : 16;
+}
+
 // One workgroup's tile: context range x (keys [x KS, (x+1) KS)), query tile qt of chunk c, kv
-// head g.  Rows are absolute rows of q / out; partials are indexed from row_base.
+// head g.  Rows are absolute rows of q / out; partials are indexed from row_base.  ring0..3 are
+// the LDS stage buffers (prefill_stage_bytes each); wide0 / wide1 the widened fp8 stages
+// (prefill_widened_bytes each).
 template <int KIND, int D, int BS, int NT>
 __device__ __forceinline__ void prefill_tile(
-    char* ring0, char* ring1, char* ring2, char* ring3, int x, int qt, int c, int g,
+    char* ring0, char* ring1, char* ring2, char* ring3, char* wide0, char* wide1, int x, int qt,
+    int c, int g,
     long long row_base, void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ qsl, const int32_t* __restrict__ context_lens,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int mbps, int Hq, int Hkv, int G,
     long long NB, long long total_q, int nsplit, int KS, int max_ctx, float qk_scale,
     float v_scale) {
-  using Ops = KvOps<KIND, D, BS>;
+  // fp8 tiles are staged as they are stored and widened once per stage into a bf16 copy (the
+  // widening is exact), which the matrix-core code then reads like a bf16 cache's tiles: every
+  // wavefront of the workgroup shares one conversion instead of repeating it in registers.
+  constexpr bool WIDEN = KIND == KFP8;
+  using Ops = KvOps<WIDEN ? KBF16 : KIND, D, BS>;  // operands as the matrix cores read them
+  using OpsS = KvOps<KIND, D, BS>;                  // tiles as they are stored and staged
   constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
   constexpr int TILE = Ops::TILE;
+  constexpr int NLS = OpsS::NL, TILE_S = OpsS::TILE;
   constexpr int SK = stage_keys(KIND);   // keys per stage
   constexpr int SF = SK / BS;            // frames per stage
   constexpr int NG = SF * KG;            // 16-key groups per stage
-  constexpr int STAGE = SF * 2 * TILE;   // bytes of K and V per stage
+  constexpr int STAGE = SF * 2 * TILE_S; // bytes of K and V per staged stage
   static_assert(NG % 2 == 0, "a stage is pairs of 16-key groups");
+  static_assert(!WIDEN || (TILE == 2 * TILE_S && NL == 2 * NLS), "fp8 widens to twice the bytes");
   constexpr int QB = PQ<KIND>::bytes;
 
   static_assert(STAGE == prefill_stage_bytes<KIND, D, BS>(), "stage size");
@@ -195,7 +212,7 @@ __device__ __forceinline__ void prefill_tile(
     for (int k = 0; k < BPW; ++k) {
       const int blk = w + k * kPWaves;
       if (NBLK < kPWaves && blk >= NBLK) break;  // wavefront-uniform
-      const int fl = blk / (2 * NL), kind = (blk / NL) & 1, r = blk % NL;
+      const int fl = blk / (2 * NLS), kind = (blk / NLS) & 1, r = blk % NLS;
       int t = tix[0];
 #pragma unroll
       for (int z = 1; z < SF; ++z)
@@ -203,7 +220,7 @@ __device__ __forceinline__ void prefill_tile(
       // frames past the range and invalid ids copy 16 bytes of tile 0 into every lane's slot
       // (never used): every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      const char* src = base + (size_t)(uint32_t)max(t, 0) * TILE + r * 1024 + (t >= 0 ? lane16 : 0);
+      const char* src = base + (size_t)(uint32_t)max(t, 0) * TILE_S + r * 1024 + (t >= 0 ? lane16 : 0);
       lds_dma16(src, buf_lds + blk * 1024);
     }
     if (next) {
@@ -355,17 +372,54 @@ __device__ __forceinline__ void prefill_tile(
   // st run on the vector ALUs, the score MFMAs of stage st + 1 are already issued and the copies
   // of stages st + 2 and st + 3 are in flight.  Stage st + 3 goes into the buffer of stage st - 1,
   // which every wavefront finished reading before the previous meeting point.
+  //
+  // fp8: a staged stage is widened into the bf16 buffer wide[st % 2] by all wavefronts together
+  // (wavefront w takes blocks w, w + 8, ...).  A lane's 16 bytes of fp8 block r of a K or V tile
+  // widen, in order, to its 16 bytes of bf16 blocks 2r and 2r + 1 of the same tile in the bf16
+  // layout.  Stage st + 1 is widened at the start of stage st: its copies landed before the
+  // previous meeting point, and the buffer it overwrites held stage st - 1, which every wavefront
+  // finished reading before that meeting point.  A second meeting point then publishes it.
+  auto widen = [&](const char* staged, char* wide) {
+    if constexpr (WIDEN) {
+      constexpr int WPW = (NBLK + kPWaves - 1) / kPWaves;  // blocks per wavefront
+#pragma unroll
+      for (int k = 0; k < WPW; ++k) {
+        const int blk = w + k * kPWaves;
+        if (NBLK < kPWaves && blk >= NBLK) break;  // wavefront-uniform
+        const int fl = blk / (2 * NLS), kind = (blk / NLS) & 1, r = blk % NLS;
+        const u32x4 x8 = *((const u32x4*)(staged + blk * 1024) + lane);
+        const u32x2 a = fp8x4_to_bf16x4(x8[0]), b = fp8x4_to_bf16x4(x8[1]);
+        const u32x2 c2 = fp8x4_to_bf16x4(x8[2]), d2 = fp8x4_to_bf16x4(x8[3]);
+        char* dst = wide + (2 * fl + kind) * TILE + 2 * r * 1024;
+        *((u32x4*)dst + lane) = (u32x4){a[0], a[1], b[0], b[1]};
+        *((u32x4*)(dst + 1024) + lane) = (u32x4){c2[0], c2[1], d2[0], d2[1]};
+      }
+    }
+  };
+  auto publish = [&]() {
+    if constexpr (WIDEN) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  };
   dma(ring0, 0);
   dma(ring1, 1);
   dma(ring2, 2);
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   f32x4 sa[NT][NG], sz[NT][NG];
-  qk(ring0, sa, 0, SF);
+  widen(ring0, wide0);
+  publish();
+  qk(WIDEN ? wide0 : ring0, sa, 0, SF);
   // one stage: copy stage st + 3 into the buffer stage st - 1 used, finish stage st (its scores
   // in s_cur) while the scores of stage st + 1 go into s_nxt, meet
   auto stage = [&](int st, const char* cur, const char* nxt, char* free_buf, f32x4 (&s_cur)[NT][NG],
                    f32x4 (&s_nxt)[NT][NG]) {
     dma(free_buf, st + 3);
+    if constexpr (WIDEN) {
+      char* wcur = (st & 1) ? wide1 : wide0;
+      char* wnxt = (st & 1) ? wide0 : wide1;
+      widen(nxt, wnxt);
+      publish();
+      cur = wcur;
+      nxt = wnxt;
+    }
     // (past the last stage the next-stage scores read a buffer already written and are never
     // used: issuing them unconditionally keeps them in the exponentials' block)
     // the next stage's frames scored while pair pp of this stage is finished
