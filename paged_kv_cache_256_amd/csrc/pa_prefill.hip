@@ -16,7 +16,7 @@
 //    stage; the copies of the next two stages stay in flight across it.  The block ids come in
 //    windows of 64 frames (one vector load, a window ahead) and are turned into tile indices once
 //    per window, so issuing a stage's copies costs a few scalar instructions per block and never
-//    waits for memory.
+//    waits for memory.  fp8 stages are widened to bf16 once, in LDS, by the whole workgroup.
 //  * Online softmax per query row (causal mask on the diagonal stages), O^T += V^T P^T with
 //    16x16x32 products over pairs of 16-key groups; each pair also issues its part of the next
 //    stage's score MFMAs, so the matrix cores work beside the exponentials.
