@@ -301,6 +301,34 @@ def test_one_token_and_identical_keys_closed_forms_on_gpu():
         np.testing.assert_array_equal(o[1, h], vrows[0, h // G].double().numpy())
 
 
+# The decode launch is sized from the host-known bound B Hkv (ceil(max_context_len / bs) + 4) at
+# 32 units per wavefront (whole workgroups of 4, at most 3 per compute unit): these batches give
+# launches from the smallest through intermediate sizes, with lengths that cut runs at many
+# wavefront boundaries.
+LAUNCH_SIZE_CASES = [
+    # (B, longest length drawn, G): launches of 4, 8, 52, 256 and 636 wavefronts
+    (1, 40, 8),
+    (3, 700, 8),
+    (9, 1500, 8),
+    (24, 3000, 8),
+    (40, 4096, 8),
+]
+
+
+@pytest.mark.parametrize("B,maxlen,G", LAUNCH_SIZE_CASES,
+                         ids=[f"B{c[0]}-L{c[1]}" for c in LAUNCH_SIZE_CASES])
+def test_decode_launch_sizes(B, maxlen, G):
+    Hkv = 2
+    _say(f"decode launch-size case B={B} max length {maxlen}")
+    c = workloads.decode_case("launch-size", 900 + B, Hq=G * Hkv, Hkv=Hkv, D=128, bs=16,
+                              lens=lambda rng: rng.integers(1, maxlen + 1, size=B),
+                              kv_dtype="bf16", std=0.7071)
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_caches(g, o)
+    _check_decode(g, o)
+
+
 STREAM_CASES = [
     # (name, Hq, Hkv, kv, bs, lengths): extremes of the batch-wide stream split
     ("one-sequence-over-every-wavefront", 8, 1, "bf16", 16, [100000]),
