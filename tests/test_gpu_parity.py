@@ -471,3 +471,44 @@ def test_prepared_calls_match_ordinary_calls_bit_for_bit():
     _, m1 = g.mixed(mode="split")
     torch.cuda.synchronize()
     assert torch.equal(m1, m0)
+
+
+def test_empty_calls_are_no_ops():
+    """Every entry point accepts an empty batch (no tokens, sequences, chunks or copy pairs):
+    the call succeeds, writes nothing, and the next non-empty call on the stream is unaffected."""
+    _say("empty calls")
+    dev = device()
+    NB, Hkv, Hq, D, bs = 8, 2, 4, 128, 16
+    kc, vc = pa.new_kv_cache(NB, Hkv, bs, D, "bf16", device=dev)
+    kc.fill_(1.5)
+    vc.fill_(-2.5)
+    before_k, before_v = to_raw(kc).copy(), to_raw(vc).copy()
+    none_rows = torch.empty(0, Hkv, D, dtype=torch.bfloat16, device=dev)
+    pa.reshape_and_cache(none_rows, none_rows, kc, vc,
+                         torch.empty(0, dtype=torch.int64, device=dev), block_size=bs,
+                         kv_dtype="bf16")
+    pa.copy_blocks(kc, vc, torch.empty(0, 2, dtype=torch.int64, device=dev), block_size=bs,
+                   kv_dtype="bf16")
+    q0 = torch.empty(0, Hq, D, dtype=torch.bfloat16, device=dev)
+    bt0 = torch.empty(0, 4, dtype=torch.int32, device=dev)
+    lens0 = torch.empty(0, dtype=torch.int32, device=dev)
+    assert pa.decode_workspace_bytes(0, Hq, D, bs, "bf16", 64) == 0
+    out = pa.decode(q0, kc, vc, bt0, lens0, block_size=bs, scale=0.1, kv_dtype="bf16",
+                    max_context_len=64)
+    assert out.shape == (0, Hq, D)
+    qsl0 = torch.zeros(1, dtype=torch.int32, device=dev)
+    pa.prefill_chunk(q0, kc, vc, bt0, qsl0, lens0, block_size=bs, scale=0.1, kv_dtype="bf16",
+                     max_chunk_len=16, max_context_len=64)
+    for mode in ("auto", "split", "separate"):
+        pa.mixed_attention(q0, kc, vc, bt0, qsl0, lens0, 0, block_size=bs, scale=0.1,
+                           kv_dtype="bf16", max_chunk_len=16, max_context_len=64, mode=mode)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_raw(kc), before_k)
+    np.testing.assert_array_equal(to_raw(vc), before_v)
+    # a one-token decode right after: the output is that token's V row (closed form)
+    q1 = torch.randn(1, Hq, D, device=dev).to(torch.bfloat16)
+    bt1 = torch.tensor([[3, 0, 0, 0]], dtype=torch.int32, device=dev)
+    out1 = pa.decode(q1, kc, vc, bt1, torch.tensor([1], dtype=torch.int32, device=dev),
+                     block_size=bs, scale=0.1, kv_dtype="bf16", max_context_len=64)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(out_f64(out1), np.full((1, Hq, D), -2.5))
