@@ -105,7 +105,7 @@ def decode(**kw):
     (dict(bt=NULL), EINVAL, "null pointer"),
     (dict(B=-1), EINVAL, "bad sizes"),
     (dict(NB=0), EINVAL, "bad sizes"),
-    (dict(B=70000), ENOTSUP, "batch"),
+    (dict(B=65536), ENOTSUP, "batch"),  # one past the largest batch a call takes
     (dict(Hq=6, Hkv=4), EINVAL, "multiple"),
     (dict(Hq=6, Hkv=2), ENOTSUP, "query heads per kv head"),
     (dict(Hq=64, Hkv=2), ENOTSUP, "query heads per kv head"),

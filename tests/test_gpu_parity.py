@@ -356,6 +356,19 @@ def test_decode_stream_split_extremes(name, Hq, Hkv, kv, bs, lens):
     _check_decode(g, o)
 
 
+def test_decode_at_the_largest_batch_one_call_takes():
+    """65,535 sequences (the most one pa_decode call accepts) of 1-40 tokens, planned by the
+    separate plan kernel: every cache slot bit-exact and every output against the oracle."""
+    _say("max batch 65535")
+    c = workloads.decode_case("max-batch", 11, Hq=4, Hkv=1, D=64, bs=16,
+                              lens=lambda rng: rng.integers(1, 41, size=65535), kv_dtype="bf16",
+                              std=0.7071, pool="scattered")
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_caches(g, o)
+    _check_decode(g, o)
+
+
 def test_graph_replays_match_eager_bits():
     """A step captured in a HIP graph (copies, cache writes, prefill chunk, decode, and the mixed
     step in its single-kernel mode) and replayed several times, with eager work between the
