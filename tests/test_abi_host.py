@@ -168,6 +168,7 @@ def prefill(**kw):
     (dict(mcl=200, mctx=100), EINVAL, "max_chunk_len"),
     (dict(mcl=0), EINVAL, "max_chunk_len"),
     (dict(nc=40000, Hkv=2), ENOTSUP, "num_chunks * Hkv"),
+    (dict(nc=8192, Hq=16, Hkv=8), ENOTSUP, "num_chunks * Hkv"),  # 65,536: one past the limit
     (dict(tq=1 << 31), ENOTSUP, "total_q"),
     (dict(D=256), ENOTSUP, "head_dim"),
     (dict(qd=F32, kvd=FP8), ENOTSUP, "dtype combination"),
@@ -301,6 +302,7 @@ def mixed(**kw):
     (dict(mcl=200, mctx=100), EINVAL, "max_chunk_len"),
     (dict(mctx=0), EINVAL, "max_context_len"),
     (dict(nc=40000, Hkv=2), ENOTSUP, "num_chunks * Hkv"),
+    (dict(nc=8192, Hq=16, Hkv=8), ENOTSUP, "num_chunks * Hkv"),  # 65,536: one past the limit
     (dict(tq=1 << 31), ENOTSUP, "total_q"),
     (dict(D=256), ENOTSUP, "head_dim"),
     (dict(Hq=6, Hkv=4), EINVAL, "multiple"),

@@ -139,6 +139,24 @@ def test_prefill_ranges_spanning_several_id_windows(kv, bs, G, L):
     assert err <= tolerance(c), f"prefill max abs err {err:.3e}"
 
 
+def test_prefill_at_the_most_chunks_one_call_takes():
+    """8,191 chunks of 1-16 rows over 8 kv heads (num_chunks x Hkv = 65,528, next to the call's
+    limit of 65,535), each over a context of up to 60 earlier tokens: every output row."""
+    _say("prefill with 8191 chunks")
+    rng = np.random.default_rng(3)
+    C = rng.integers(1, 17, size=8191)
+    L = C + rng.integers(0, 61, size=8191)
+    c = workloads.chunk_case("max-chunks", 13, Hq=16, Hkv=8, D=64, bs=16, chunks=list(zip(C, L)),
+                             decode_lens=[], kv_dtype="bf16", std=0.7071)
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_caches(g, o)
+    got = out_f64(g.chunk_out)
+    assert np.isfinite(got).all()
+    err = np.abs(got - o.prefill()).max()
+    assert err <= tolerance(c), f"prefill max abs err {err:.3e}"
+
+
 def test_copy_blocks_bit_exact_and_shared_equals_private():
     c = workloads.cases.fork_case("fork", 31, prompts=3, branches=4, prompt_len=64, tail_lo=3,
                                   tail_hi=70, Hq=16, Hkv=2, D=128, bs=32, kv_dtype="fp8")
