@@ -239,7 +239,8 @@ def main():
         block_manager_bench()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1", file=sys.stderr)
+        print("bench.py: the library has no multi-GPU path and measures one GPU; --gpus must be 1",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -75,7 +75,7 @@ enum {
   PA_OK = 0,
   PA_EINVAL = -1,  /* null pointer, bad size, or an index array that fails validation */
   PA_ERANGE = -2,  /* a value outside its allowed range (validators) */
-  PA_ENOTSUP = -3, /* a shape or dtype combination this build does not implement */
+  PA_ENOTSUP = -3, /* a shape or dtype combination the library does not implement */
   PA_EHIP = -4,    /* a HIP runtime call or kernel launch failed */
   PA_ENOSPC = -5   /* the workspace is smaller than the *_workspace_bytes result */
 };
