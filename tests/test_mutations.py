@@ -64,14 +64,34 @@ def _positions_transposed(kind, bs, D, dtype):
     return pos.T.reshape(bs, D) if kind == "v" else pos
 
 
+def _dequant_divides(cache, table_row, Lq, kind, *, bs, kv_dtype, scale=1.0):
+    vals = _ORIG_GATHER(cache, table_row, Lq, kind, bs=bs, kv_dtype=kv_dtype, scale=1.0)
+    return vals / float(np.float32(scale)) if kv_dtype == "fp8" else vals
+
+
+def _dequant_twice(cache, table_row, Lq, kind, *, bs, kv_dtype, scale=1.0):
+    vals = _ORIG_GATHER(cache, table_row, Lq, kind, bs=bs, kv_dtype=kv_dtype, scale=scale)
+    return vals * float(np.float32(scale)) if kv_dtype == "fp8" else vals
+
+
+def _decode_swaps_scales(*args, k_scale=1.0, v_scale=1.0, **kw):
+    return _ORIG_DECODE(*args, k_scale=v_scale, v_scale=k_scale, **kw)
+
+
+def _chunk_swaps_scales(*args, k_scale=1.0, v_scale=1.0, **kw):
+    return _ORIG_CHUNK(*args, k_scale=v_scale, v_scale=k_scale, **kw)
+
+
 _ORIG_GATHER = P.gather_kv
+_ORIG_DECODE = P.decode
+_ORIG_CHUNK = P.prefill_chunk
 _ORIG_ENC = N.e4m3fn_encode
 _ORIG_ATTEND = P._softmax_attend
 _ORIG_POS = L.tile_positions
 
 MUTANTS = [
     ("slot offset off by one", P, "slot_of", _slot_off_by_one,
-     [pins.test_allocate_slot_semantics_give_slot_of]),
+     [pins.test_slot_of_follows_the_block_split_rule]),
     ("gather ignores the block table", P, "gather_kv", _gather_ignores_table,
      [lambda: pins.test_diagram_block_tables("block_table_codebumble")]),
     ("softmax normalised by its max", P, "_softmax_attend", _softmax_max_normalised,
@@ -87,6 +107,15 @@ MUTANTS = [
      [pins.test_e4m3fn_encode_ties_saturation_nan]),
     ("V tile layout transposed", L, "tile_positions", _positions_transposed,
      [pins.test_tile_layout_hand_evaluated_entries]),
+    ("fp8 codes divided by the scale", P, "gather_kv", _dequant_divides,
+     [pins.test_fp8_one_token_output_is_code_value_times_v_scale,
+      pins.test_fp8_store_then_gather_round_trips_with_distinct_scales]),
+    ("fp8 scale applied twice", P, "gather_kv", _dequant_twice,
+     [pins.test_fp8_two_token_softmax_depends_on_k_scale]),
+    ("k_scale and v_scale swapped in decode", P, "decode", _decode_swaps_scales,
+     [pins.test_fp8_one_token_output_is_code_value_times_v_scale]),
+    ("k_scale and v_scale swapped in the chunk", P, "prefill_chunk", _chunk_swaps_scales,
+     [pins.test_fp8_two_row_chunk_closed_form]),
 ]
 
 
@@ -100,7 +129,7 @@ def test_planted_mistake_is_caught(monkeypatch, name, mod, attr, bad, checks):
         import oracle
         monkeypatch.setattr(pins, "tile_positions", bad)
         monkeypatch.setattr(oracle, attr, bad)
-    if mod is P and attr in ("slot_of",):
+    if mod is P and attr in ("slot_of", "gather_kv", "decode", "prefill_chunk"):
         import oracle
         monkeypatch.setattr(oracle, attr, bad)
     if attr == "bf16_bits_to_f64":

@@ -192,37 +192,28 @@ def test_pack_unpack_round_trip():
 # ----------------------------------------------------------------------------- block tables and slots
 
 
-class _PageManager:
-    """The page's conceptual block-table manager (codebumble.net, "The Block Table Mapping
-    Subsystem"), written out: a FIFO free list, a new frame taken from its head whenever a
-    sequence's next position is the first slot of a block."""
-
-    def __init__(self, block_size, num_physical_blocks):
-        self.block_size = block_size
-        self.free = list(range(num_physical_blocks))
-        self.tables = {}
-
-    def allocate_slot(self, rid, seq_len):
-        lb, off = seq_len // self.block_size, seq_len % self.block_size
-        self.tables.setdefault(rid, [])
-        if off == 0:
-            self.tables[rid].append(self.free.pop(0))
-        return self.tables[rid][lb]
-
-
-def test_allocate_slot_semantics_give_slot_of():
+def test_slot_of_follows_the_block_split_rule():
+    """codebumble.net, "The Block Table Mapping Subsystem": a position's logical block is
+    position // block_size and its offset position % block_size, and a sequence takes the next
+    frame from the head of a FIFO free list whenever it opens a block.  The frames that rule
+    hands out are written here in closed form instead of being simulated."""
     g = _golden("page_examples.json")["allocate_slot"]
-    m = _PageManager(g["block_size"], g["num_physical_blocks"])
-    # two sequences growing in lockstep: frames interleave in allocation order
-    for pos in range(40):
-        for rid in ("a", "b"):
-            frame = m.allocate_slot(rid, pos)
-            table = np.array(m.tables[rid])
-            assert oracle.slot_of(table, [pos], g["block_size"])[0] == frame * 16 + pos % 16
-    m1 = _PageManager(g["block_size"], g["num_physical_blocks"])
+    bs = g["block_size"]
+    # one sequence of 48 tokens from a fresh pool opens blocks 0, 1, 2 and takes frames 0, 1, 2
+    table = np.array(g["first_sequence_frames"], dtype=np.int32)
     for pos in range(48):
-        m1.allocate_slot("x", pos)
-    assert m1.tables["x"] == g["first_sequence_frames"]
+        assert oracle.slot_of(table, [pos], bs)[0] == [0, 1, 2][pos // 16] * 16 + pos % 16
+    # two sequences r = 0, 1 growing in lockstep open their j-th blocks one after the other, so
+    # sequence r's block j holds frame 2 j + r
+    for r in (0, 1):
+        tab = np.array([2 * j + r for j in range(3)], dtype=np.int32)
+        pos = np.arange(40)
+        want = (2 * (pos // 16) + r) * 16 + pos % 16
+        np.testing.assert_array_equal(oracle.slot_of(tab, pos, bs), want)
+    # a vector of positions is split element by element, and int64 holds slots past 2^31
+    big = np.array([2 ** 27, 5], dtype=np.int32)
+    assert oracle.slot_of(big, [3], bs)[0] == 2 ** 31 + 3
+    assert oracle.slot_of(big, [17], bs)[0] == 5 * 16 + 1
 
 
 @pytest.mark.parametrize("which", ["block_table_codebumble", "block_table_bicarait"])
@@ -345,6 +336,107 @@ def _brute_decode(q, K, V, scale):
         for d in range(D):
             out[h][d] = sum(w[t] * float(V[t, g, d]) for t in range(L)) / z
     return np.array(out)
+
+
+# ----------------------------------------------------------------------------- fp8 dequantisation
+#
+# infoisland, section 4 ("--kv-cache-dtype fp8"): the cache stores one e4m3fn code per element,
+# and the per-tensor K and V scales turn a code back into a value as code value x scale.  The
+# expected values below are written by hand from the code table (0x30 = 0.5, 0x38 = 1, 0x3C =
+# 1.5, 0x40 = 2, 0x48 = 4, 0xB8 = -1, 0xC0 = -2, 0x01 = 2^-9) and the scales, not computed by
+# the reference's own gather.
+
+
+def _fp8_cache_with_rows(rows, kind, *, bs=32, D=64, NB=3, frame=1, fill=0x00):
+    """An fp8 cache of NB frames, one kv head, whose frame `frame` holds token t's row of codes
+    rows[t] (a length-D list, or one code for the whole row); other slots hold `fill`."""
+    vals = np.full((NB, 1, bs, D), fill, dtype=np.uint8)
+    for t, r in enumerate(rows):
+        vals[frame, 0, t, :] = r
+    return oracle.pack_tiles(vals, kind, "fp8").reshape(NB, 1, bs * D)
+
+
+def test_fp8_one_token_output_is_code_value_times_v_scale():
+    D = 64
+    vrow = [0x3C, 0xC0, 0x30, 0x01] + [0x38] * (D - 4)
+    kc = _fp8_cache_with_rows([[0x40] * D], "k", fill=0x7E)
+    vc = _fp8_cache_with_rows([vrow], "v", fill=0x7E)
+    q = np.random.default_rng(21).standard_normal((1, 2, D)).astype(np.float32)
+    out = oracle.decode(q, kc, vc, np.array([[1]]), np.array([1]), scale=0.125, bs=32,
+                        q_dtype="f32", kv_dtype="fp8", k_scale=3.0, v_scale=0.25)
+    want = [0.375, -0.5, 0.125, 2.0 ** -11] + [0.25] * (D - 4)
+    for h in range(2):
+        assert out[0, h].tolist() == want
+
+
+def _two_token_fp8_case():
+    D = 64
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, 0] = 1.0
+    kc = _fp8_cache_with_rows([[0x38] + [0x00] * (D - 1), [0x40] + [0x00] * (D - 1)], "k",
+                              fill=0x7E)
+    vc = _fp8_cache_with_rows([0x38, 0x48], "v", fill=0x7E)
+    return q, kc, vc
+
+
+def test_fp8_two_token_softmax_depends_on_k_scale():
+    # k_scale 0.5: keys 1 and 2 score 0.5 and 1.0, so the second token weighs 1 / (1 + e^-0.5);
+    # v_scale 0.125: values 1 and 4 become 0.125 and 0.5.
+    q, kc, vc = _two_token_fp8_case()
+    out = oracle.decode(q, kc, vc, np.array([[1]]), np.array([2]), scale=1.0, bs=32,
+                        q_dtype="f32", kv_dtype="fp8", k_scale=0.5, v_scale=0.125)
+    want = 0.125 + 0.375 / (1.0 + math.exp(-0.5))
+    assert abs(want - 0.35842224920069548) < 1e-15
+    np.testing.assert_allclose(out[0, 0], np.full(64, want), rtol=0, atol=1e-15)
+
+
+def test_fp8_two_row_chunk_closed_form():
+    # The same two tokens as one causal chunk of two rows (bicarait.com, "Architectural
+    # Blueprint 3"): row 0 sees only the first token and returns its value 0.125; row 1 sees
+    # both, as in the decode case above.
+    q, kc, vc = _two_token_fp8_case()
+    q2 = np.concatenate([q, q], axis=0)
+    out = oracle.prefill_chunk(q2, kc, vc, np.array([[1]]), np.array([0, 2]), np.array([2]),
+                               scale=1.0, bs=32, q_dtype="f32", kv_dtype="fp8", k_scale=0.5,
+                               v_scale=0.125)
+    assert out[0, 0].tolist() == [0.125] * 64
+    np.testing.assert_allclose(out[1, 0], 0.125 + 0.375 / (1.0 + math.exp(-0.5)), rtol=0,
+                               atol=1e-15)
+
+
+def test_fp8_identical_keys_mean_of_values_times_v_scale():
+    # Five tokens with the same key codes: every weight is 1/5, so the output is
+    # 0.75 x mean(1, 2, 0.5, 1.5, -1) = 0.75 x 0.8 = 0.6 in every column.
+    D = 64
+    key = np.random.default_rng(22).integers(0, 0x7E, D).astype(np.uint8)
+    kc = _fp8_cache_with_rows([key] * 5, "k", fill=0x7E)
+    vc = _fp8_cache_with_rows([0x38, 0x40, 0x30, 0x3C, 0xB8], "v", fill=0x7E)
+    q = np.random.default_rng(23).standard_normal((1, 4, D)).astype(np.float32)
+    out = oracle.decode(q, kc, vc, np.array([[1]]), np.array([5]), scale=0.3, bs=32,
+                        q_dtype="f32", kv_dtype="fp8", k_scale=2.0, v_scale=0.75)
+    np.testing.assert_allclose(out[0], np.full((4, D), 0.6), rtol=0, atol=1e-15)
+
+
+def test_fp8_store_then_gather_round_trips_with_distinct_scales():
+    # Rows stored with k_scale and v_scale (x / scale, rounded to a code) and read back (code x
+    # scale) come back within the e4m3fn rounding bound: 2^-4 relative for normal codes, half
+    # the subnormal step 2^-10 times the scale absolute.
+    rng = np.random.default_rng(24)
+    Hkv, D, bs, L = 2, 64, 32, 40
+    k = (rng.standard_normal((L, Hkv, D)) * 3.0).astype(np.float32)
+    v = (rng.standard_normal((L, Hkv, D)) * 0.02).astype(np.float32)
+    ks, vs = float(np.abs(k).max() / 448), float(np.abs(v).max() / 448)
+    assert vs < ks / 50
+    kc = oracle.new_cache(4, Hkv, bs, D, "fp8")
+    vc = oracle.new_cache(4, Hkv, bs, D, "fp8")
+    table = np.array([3, 0], dtype=np.int32)
+    oracle.reshape_and_cache(kc, vc, k, v, oracle.slot_of(table, np.arange(L), bs), bs=bs,
+                             src_dtype="f32", kv_dtype="fp8", k_scale=ks, v_scale=vs)
+    for x, c, kind, s in ((k, kc, "k", ks), (v, vc, "v", vs)):
+        back = oracle.gather_kv(c, table, L, kind, bs=bs, kv_dtype="fp8", scale=s)
+        x64 = x.astype(np.float64)
+        bound = np.abs(x64) * 2.0 ** -4 + 2.0 ** -10 * s
+        assert np.all(np.abs(back - x64) <= bound)
 
 
 def test_brute_force_every_injective_table():
