@@ -149,6 +149,19 @@ def _dev(t: torch.Tensor, name: str, dtype=None, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _need_rows(t: torch.Tensor, name: str, n: int, exact: bool = True):
+    """The index tensor t must have n rows (exact) or at least n rows: the library reads that
+    many and trusts the caller for the rest."""
+    have = t.shape[0] if t.dim() else 1
+    if (have != n) if exact else (have < n):
+        raise ValueError(f"{name} has {have} rows, the call needs {'' if exact else 'at least '}{n}")
+
+
+def _need_out_like(out: torch.Tensor, q: torch.Tensor):
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have the shape of q {tuple(q.shape)}, got {tuple(out.shape)}")
+
+
 def _cache_geometry(k_cache, v_cache, block_size, kv_dtype):
     if k_cache.shape != v_cache.shape or k_cache.dim() != 3:
         raise ValueError("k_cache and v_cache must both be [NB, Hkv, block_size*D]")
@@ -174,6 +187,9 @@ def reshape_and_cache(k, v, k_cache, v_cache, slot_mapping, *, block_size: int, 
     T = k.shape[0]
     if tuple(k.shape) != (T, Hkv, D) or tuple(v.shape) != (T, Hkv, D):
         raise ValueError(f"k, v must be [T, {Hkv}, {D}]")
+    if slot_mapping.dim() != 1:
+        raise ValueError("slot_mapping must be one-dimensional")
+    _need_rows(slot_mapping, "slot_mapping", T)
     args = (_dev(k, "k"), _dev(v, "v"), _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
             _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
             _dev(slot_mapping, "slot_mapping", torch.int64, 1), T, NB, Hkv, D, block_size,
@@ -214,8 +230,11 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, 
     B, Hq, Dq = q.shape
     if Dq != D:
         raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    _need_rows(block_tables, "block_tables", B, exact=False)
+    _need_rows(context_lens, "context_lens", B)
     if out is None:
         out = torch.empty_like(q)
+    _need_out_like(out, q)
     need = decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -254,8 +273,11 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, query_start_loc, context_le
     if Dq != D:
         raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
     num_chunks = context_lens.shape[0]
+    _need_rows(query_start_loc, "query_start_loc", num_chunks + 1)
+    _need_rows(block_tables, "block_tables", num_chunks, exact=False)
     if out is None:
         out = torch.empty_like(q)
+    _need_out_like(out, q)
     need = prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq,
                                          Hkv, D, block_size, kv_dtype)
     if need:
@@ -323,8 +345,10 @@ def mixed_attention(q, k_cache, v_cache, block_tables, query_start_loc, context_
     if num_chunks < 0 or query_start_loc.shape[0] != context_lens.shape[0] + 1:
         raise ValueError("query_start_loc must have one entry more than context_lens, which "
                          "covers the decodes and the chunks")
+    _need_rows(block_tables, "block_tables", context_lens.shape[0], exact=False)
     if out is None:
         out = torch.empty_like(q)
+    _need_out_like(out, q)
     need = mixed_workspace_bytes(num_decodes, num_chunks, total_q, max_chunk_len, max_context_len,
                                  Hq, Hkv, D, block_size, kv_dtype)
     if need:

@@ -459,7 +459,8 @@ int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_se
                               int max_chunk_len, int max_context_len) {
   if (num_decodes < 0 || num_chunks < 0 || max_blocks_per_seq < 1 || block_size < 1 || NB < 1)
     return fail(PA_EINVAL, "bad sizes");
-  if (num_decodes + num_chunks > 0 && (!block_tables || !query_start_loc || !context_lens))
+  if (num_decodes + num_chunks == 0) return PA_OK;  // nothing to check, and nothing is read
+  if (!block_tables || !query_start_loc || !context_lens)
     return fail(PA_EINVAL, "null pointer argument");
   for (int b = 0; b <= num_decodes; ++b)
     if (query_start_loc[b] != b)

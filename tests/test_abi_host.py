@@ -396,3 +396,50 @@ def test_workspaces_must_be_256_byte_aligned():
     assert need > 0
     assert prefill(nc=1, tq=512, mcl=512, mctx=16384, Hq=32, Hkv=8, D=128, ws=odd,
                    wsb=need) == EINVAL and "aligned" in err()
+
+
+def test_binding_rejects_index_tensors_of_the_wrong_size():
+    # The size checks run before any device check, so CPU tensors reach them: a mismatched
+    # index tensor would make the kernels read or write past a buffer.
+    import torch
+    bf = torch.bfloat16
+    kc = torch.zeros(8, 2, 16 * 64, dtype=bf)
+    vc = torch.zeros_like(kc)
+    k = torch.zeros(5, 2, 64, dtype=bf)
+    with pytest.raises(ValueError, match="slot_mapping has 4 rows, the call needs 5"):
+        pa.reshape_and_cache(k, k, kc, vc, torch.zeros(4, dtype=torch.int64), block_size=16,
+                             kv_dtype="bf16")
+    with pytest.raises(ValueError, match="one-dimensional"):
+        pa.reshape_and_cache(k, k, kc, vc, torch.zeros(5, 1, dtype=torch.int64), block_size=16,
+                             kv_dtype="bf16")
+    q = torch.zeros(3, 4, 64, dtype=bf)
+    bt = torch.zeros(3, 2, dtype=torch.int32)
+    cl = torch.ones(3, dtype=torch.int32)
+    kw = dict(block_size=16, scale=0.125, kv_dtype="bf16", max_context_len=32)
+    with pytest.raises(ValueError, match="block_tables has 2 rows, the call needs at least 3"):
+        pa.decode(q, kc, vc, bt[:2], cl, **kw)
+    with pytest.raises(ValueError, match="context_lens has 4 rows, the call needs 3"):
+        pa.decode(q, kc, vc, bt, torch.ones(4, dtype=torch.int32), **kw)
+    with pytest.raises(ValueError, match="out must have the shape of q"):
+        pa.decode(q, kc, vc, bt, cl, out=torch.zeros(2, 4, 64, dtype=bf), **kw)
+    ckw = dict(block_size=16, scale=0.125, kv_dtype="bf16", max_chunk_len=3, max_context_len=32)
+    qsl = torch.tensor([0, 3], dtype=torch.int32)
+    c1 = torch.tensor([20], dtype=torch.int32)
+    with pytest.raises(ValueError, match="query_start_loc has 3 rows, the call needs 2"):
+        pa.prefill_chunk(q, kc, vc, bt, torch.tensor([0, 1, 3], dtype=torch.int32), c1, **ckw)
+    with pytest.raises(ValueError, match="block_tables has 0 rows"):
+        pa.prefill_chunk(q, kc, vc, bt[:0], qsl, c1, **ckw)
+    with pytest.raises(ValueError, match="out must have the shape of q"):
+        pa.prefill_chunk(q, kc, vc, bt, qsl, c1, out=torch.zeros(3, 4, 32, dtype=bf), **ckw)
+    mkw = dict(block_size=16, scale=0.125, kv_dtype="bf16", max_chunk_len=2, max_context_len=32)
+    mq = torch.tensor([0, 1, 3], dtype=torch.int32)
+    ml = torch.tensor([5, 20], dtype=torch.int32)
+    with pytest.raises(ValueError, match="block_tables has 1 rows, the call needs at least 2"):
+        pa.mixed_attention(q, kc, vc, bt[:1], mq, ml, 1, **mkw)
+    with pytest.raises(ValueError, match="out must have the shape of q"):
+        pa.mixed_attention(q, kc, vc, bt, mq, ml, 1, out=torch.zeros(3, 2, 64, dtype=bf), **mkw)
+
+
+def test_validate_mixed_indices_of_an_empty_batch_reads_nothing():
+    f = lib().pa_validate_mixed_indices
+    assert f(NULL, 1, NULL, NULL, 0, 0, 16, 8, 1, 16) == OK
