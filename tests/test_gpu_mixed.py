@@ -111,8 +111,7 @@ def test_mixed_plan_kernel_path_above_1024_decodes(mode):
     g.write()
     d, ch = g.mixed(mode=mode)
     torch.cuda.synchronize()
-    seqs = sorted(set(rng.choice(c.B, size=120, replace=False).tolist()) | {0, c.B - 1})
-    err = _check(g, o, d, ch, decode_seqs=seqs)
+    err = _check(g, o, d, ch)
     _say(f"  1100 decodes + chunk ({mode}): max abs err {err:.2e}")
 
 

@@ -130,12 +130,10 @@ def test_prefill_ranges_spanning_several_id_windows(kv, bs, G, L):
     g, o = GpuStep(c), OracleStep(c)
     g.step()
     _check_caches(g, o)
-    rng = np.random.default_rng(17)
-    rows = sorted(set(rng.choice(512, size=40, replace=False).tolist()) | {0, 31, 32, 255, 256, 511})
-    got = out_f64(g.chunk_out)[rows]
+    got = out_f64(g.chunk_out)
     assert np.isfinite(got).all()
-    err = np.abs(got - o.prefill(rows)[rows]).max()
-    _say(f"  max abs err {err:.2e} over {len(rows)} rows")
+    err = np.abs(got - o.prefill()).max()
+    _say(f"  max abs err {err:.2e} over all 512 rows")
     assert err <= tolerance(c), f"prefill max abs err {err:.3e}"
 
 
