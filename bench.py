@@ -231,6 +231,9 @@ def main():
                          "per-tensor scales) -- the fp8 prefill-chunk variant")
     ap.add_argument("--chunk-block-size", type=int, default=None, choices=[16, 32],
                     help="config 5 only: the same mixed step with this block size")
+    ap.add_argument("--long", type=int, default=None, choices=[1, 4, 16],
+                    help="long-context decode instead of a named config: this many sequences of "
+                         "32,768 tokens at the 70B layer shape")
     ap.add_argument("--block-manager", action="store_true",
                     help="time the host block manager (no GPU): prompts, decode steps with their "
                          "block-table export, and copy-on-write forks, for the 70B-shape batch")
@@ -251,7 +254,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
-    if args.chunk_kv or args.chunk_block_size:
+    if args.long:
+        case = workloads.long_context(args.long)
+    elif args.chunk_kv or args.chunk_block_size:
         if args.config != 5:
             print("bench.py: --chunk-kv / --chunk-block-size apply to --config 5 only",
                   file=sys.stderr)
@@ -260,7 +265,7 @@ def main():
                                          bs=args.chunk_block_size or 16)
     else:
         case = workloads.make(args.config)
-    log(f"[bench] generated config {args.config} ({case.name}) in {time.time() - t0:.1f}s")
+    log(f"[bench] generated {case.name} in {time.time() - t0:.1f}s")
     st = DeviceState(case, dev)
     torch.cuda.synchronize()
     log(f"[bench] caches filled on the GPU ({case.NB} frames)")
@@ -421,7 +426,7 @@ def main():
         "data": "synthetic (seeded, shapes of the named layer; no weights or datasets)",
         "config": {
             "workload": case.name,
-            "cfg": args.config,
+            "cfg": case.meta.get("cfg", args.config),
             "batch": case.B,
             "q_heads": case.Hq, "kv_heads": case.Hkv, "head_dim": case.D,
             "block_size": case.bs, "kv_dtype": case.kv_dtype,

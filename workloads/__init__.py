@@ -15,6 +15,7 @@ from .cases import (  # noqa: F401
     decode_case,
     chunk_case,
     config5_variant,
+    long_context,
     fork_case,
     mixed_batch,
     MixedBatch,

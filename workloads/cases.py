@@ -431,6 +431,18 @@ def config5_variant(kv_dtype: str = "bf16", bs: int = 16, seed: int = 5) -> Deco
     return c
 
 
+def long_context(n: int, L: int = 32768, seed: int | None = None) -> DecodeCase:
+    """n sequences of L context tokens at the Llama-3-70B layer shape (64 query heads, 8 KV
+    heads, head_dim 128, bf16, 16-token blocks, values N(0,1)/sqrt(2)) over a scattered pool:
+    the long-context regime, a 32,000-token document as bicarait.com's "Architectural
+    Blueprint 3" speaks of, where a few sequences' contexts are split across the whole GPU."""
+    c = decode_case(f"llama3-70b-decode-long bf16 B{n} L{L} Hq64 Hkv8 D128 bs16",
+                    600 + n if seed is None else seed, Hq=64, Hkv=8, D=128, bs=16, lens=[L] * n,
+                    kv_dtype="bf16", std=1.0 / math.sqrt(2.0), pool="scattered")
+    c.meta["cfg"] = "long"
+    return c
+
+
 def make(cfg: int, seed: int | None = None) -> DecodeCase:
     """The five named workloads at full size (seed defaults to the config number)."""
     seed = cfg if seed is None else seed
