@@ -141,7 +141,10 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 // The host knows an upper bound of the units, B Hkv (ceil(cap / BS) + kRestart); each wavefront
 // gets at least kMinUnitsPerWave of it, so a small batch is not cut into one-frame pieces that
 // each pay the whole latency chain (plan, ids, tiles, partial, merge).
-constexpr long long kMinUnitsPerWave = 32;
+#ifndef PA_MIN_UNITS_PER_WAVE
+#define PA_MIN_UNITS_PER_WAVE 16
+#endif
+constexpr long long kMinUnitsPerWave = PA_MIN_UNITS_PER_WAVE;
 
 inline int launch_waves(int B, int Hkv, int cap, int BS) {
   const long long units = (long long)B * Hkv * ((cap + BS - 1) / BS + kRestart);

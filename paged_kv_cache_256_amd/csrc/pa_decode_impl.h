@@ -424,19 +424,28 @@ __device__ __forceinline__ void decode_stream_wave(
 
 // Merge the partials of the runs cut by wavefront range boundaries:
 // out = sum_w 2^(m_w - M) o_w / sum_w 2^(m_w - M) l_w, M = max_w m_w (the final normalised
-// reduction of codebumble.net, "CUDA Shared Memory Optimization").  One wavefront per boundary k
-// (between the ranges of wavefronts k and k + 1) looks at the run holding unit a_{k+1}: if that
-// run has frames on both sides and k is the first boundary that cuts its frames, the wavefront
-// merges the partials of wavefronts w0..w1 (those holding the run's first and last frames; any
-// with an empty range hold none) in wavefront order.  Wavefront w keeps a run in partial slot 1
-// if the run began after the start of w's range (it is then w's last run), else in slot 0.
-// Lane (row rr = lane / 4, quarter qd = lane % 4) merges D/4 outputs of query row rr; the loads
-// of kBatch partials are in flight together.
+// reduction of codebumble.net, "CUDA Shared Memory Optimization").  There is one wavefront per
+// boundary k (between the ranges of wavefronts k and k + 1); it looks at the run holding unit
+// a_{k+1}.  Every boundary w0 <= k < w1 that cuts a run sees that same run, where w0 and w1 are
+// the wavefronts holding the run's first and last frames; the run's partials are those of
+// wavefronts w0..w1 (any with an empty range hold none).  The merge is spread over those
+// boundary wavefronts by output columns: the first S of them (S a power of two, at most
+// w1 - w0 and at most D / 8) each merge a slice of D / S columns for every partial.  A run cut
+// once is merged by one wavefront; a run cut into ~100 pieces (one long sequence over the whole
+// GPU) by up to 16, each reading only its slice of the partials.  Wavefront w keeps a run in
+// partial slot 1 if the run began after the start of w's range (it is then w's last run), else
+// in slot 0.
+// Lanes: a slice's G x (D/S) outputs are held by groups of LPG lanes (row rr, QPL quads of
+// columns per lane); the 64 / LPG groups of the wavefront take the partials in turn (partial p by
+// group p mod groups), each with its own running (max, sum, accumulator), and the groups are
+// combined by the same rule with lane swaps at the end.  The merge order depends only on the
+// sizes, so equal inputs give equal bits.
 template <int KIND, int D>
 __device__ __forceinline__ void decode_reduce_wave(
     int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
-  constexpr int kBatch = 4;
+  constexpr int kBatch = 8;   // partials per group in flight together
+  constexpr int NV = D / 16;  // quads per lane at most (G = 16, one slice)
   const int U = plan[0];
   const int4 st = ((const int4*)(plan + 4))[k + 1];
   const long long F = (long long)Hkv * U;
@@ -447,42 +456,41 @@ __device__ __forceinline__ void decode_reduce_wave(
   const long long x0 = s0 + kRestart, x1 = s0 + su - 1;
   // wavefront holding unit x: the largest w with floor(F w / W) <= x
   const int w0 = (int)(((x0 + 1) * W + F - 1) / F - 1);
-  if (w0 != k) return;  // an earlier boundary cuts this run
   const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
+  const int cuts = w1 - w0;  // boundaries cutting the run's frames, k among them
+  int S = 1;
+  while (2 * S <= cuts && 2 * S <= D / 8) S *= 2;
+  const int sl = k - w0;  // this wavefront's slice
+  if (sl >= S) return;
   const int b = st.x, g = st.y;
-  // Gp = max(G, 4) rows of the group share the wavefront: lane -> (row rr, slice qd of
-  // D / lpr outputs), nv = D / (4 lpr) f32x4 per lane
-  const int Gp = G < 4 ? 4 : G;
-  const int lpr = 64 / Gp;
-  const int rr = lane / lpr, qd = lane % lpr;
-  const int nv = D / (4 * lpr);
-  constexpr int NV = D / 16;  // nv at most
+  const int cq = D / (4 * S);                  // quads of a slice row
+  const int lpr = cq < 64 / G ? cq : 64 / G;   // lanes per row in a group
+  const int qpl = cq / lpr;                    // quads per lane
+  const int lpg = G * lpr;                     // lanes per group
+  const int groups = 64 / lpg;
+  const int grp = lane / lpg, rr = (lane % lpg) / lpr, ql = lane % lpr;
+  const int col = sl * (D / S) + ql * qpl * 4;  // first output column of the lane
   float M = -INFINITY, den = 0.f;
   f32x4 num[NV];
 #pragma unroll
   for (int v = 0; v < NV; ++v) num[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  // Wavefront w0 keeps the run in slot 1 if the run began after the start of its range; every
-  // later wavefront's range starts inside the run (slot 0).  When F >= W no range is empty and
-  // wavefronts w0..w1 all hold a partial; otherwise empty ones are skipped.
   const long long aw0 = F * w0 / W;
-  const bool dense = F >= W;
-  for (int wb = w0; wb <= w1; wb += kBatch) {
+  const bool dense = F >= W;  // no empty ranges: every wavefront w0..w1 holds a partial
+  for (int wb = w0 + grp; wb <= w1; wb += kBatch * groups) {
     f32x4 ob[kBatch][NV];
     float mb[kBatch], lb[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      const int w = wb + i;
+      const int w = wb + i * groups;
       bool has = w <= w1;
       if (!dense && has) has = F * w / W < F * (w + 1) / W;
       const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
-      // rows past the group were never written: those lanes read nothing
-      const bool rd = has && rr < G;
       const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
-      const f32x4* src = (const f32x4*)(ws_o + prow * D) + qd * nv;
+      const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) ob[i][v] = (rd && v < nv) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
-      mb[i] = rd ? ws_ml[2 * prow] : -INFINITY;
-      lb[i] = rd ? ws_ml[2 * prow + 1] : 0.f;
+      for (int v = 0; v < NV; ++v) ob[i][v] = (has && v < qpl) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      mb[i] = has ? ws_ml[2 * prow] : -INFINITY;
+      lb[i] = has ? ws_ml[2 * prow + 1] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
@@ -500,12 +508,29 @@ __device__ __forceinline__ void decode_reduce_wave(
       for (int v = 0; v < NV; ++v) num[v] += ew * ob[i][v];
     }
   }
-  if (rr >= G) return;
+  // combine the groups: after the swap at distance d, each lane holds the merge of its group
+  // and the group d lanes away (lanes of one row and columns line up across groups)
+  for (int d = lpg; d < 64; d *= 2) {
+    const float M2 = __shfl_xor(M, d), den2 = __shfl_xor(den, d);
+    const float Mn = fmaxf(M, M2);
+    const float s1 = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float s2 = M2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M2 - Mn);
+    den = den * s1 + den2 * s2;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      f32x4 o2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o2[e] = __shfl_xor(num[v][e], d);
+      num[v] = num[v] * s1 + o2 * s2;
+    }
+    M = Mn;
+  }
+  if (grp != 0) return;
   const float inv = v_scale / den;
-  const size_t o = ((size_t)b * Hq + (size_t)g * G + rr) * D + (size_t)qd * nv * 4;
+  const size_t o = ((size_t)b * Hq + (size_t)g * G + rr) * D + col;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
-    if (v >= nv) break;
+    if (v >= qpl) break;
     if constexpr (KIND == KF32) {
       *(f32x4*)((float*)out + o + 4 * v) = num[v] * inv;
     } else {
