@@ -171,6 +171,25 @@ int pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_ca
                  int max_context_len, void* workspace, size_t workspace_bytes, unsigned flags,
                  void* stream);
 
+/*
+ * pa_decode_noalloc -- pa_decode_ex without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It allocates nothing: the decode's plan and partial results go to a
+ * scratch array of 16 MiB that the library holds on every GPU it runs on, from the first call
+ * on that GPU until the process ends.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (on different streams, or from different threads without
+ * ordering) race and must not be issued; calls ordered on one stream are fine.  The array keeps
+ * the last call's contents; nothing in it is read before the call writes it.  Arguments,
+ * results (bit-identical to pa_decode_ex with the same arguments) and errors are pa_decode_ex's;
+ * PA_ENOSPC when this device's launch would need more scratch than the array holds
+ * (pa_decode_workspace_bytes above 16 MiB, i.e. more than ~320 compute units at head_dim 128).
+ */
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int B, int Hq, int Hkv, int D, int block_size,
+                      int64_t NB, float scale, pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale,
+                      float v_scale, int max_context_len, unsigned flags, void* stream);
+
 /* Bytes of device workspace pa_prefill_chunk needs for these bounds (0 is a valid answer:
  * then workspace may be NULL).  The arguments are the ones pa_prefill_chunk receives. */
 size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,

@@ -6,6 +6,7 @@ declared in include/pa.h:
     reshape_and_cache  write this step's K/V rows into their cache slots
     copy_blocks        duplicate frames for copy-on-write
     decode             paged GQA decode attention (split over the context + reduce)
+    decode_noalloc     the same decode on the library's own device scratch (allocates nothing)
     prefill_chunk      causal attention of prefill chunks over their paged context
     mixed_attention    decodes and prefill chunks of one step in one persistent kernel
     BlockManager       host-side frames, block tables, slots and copy-on-write pairs
@@ -20,6 +21,7 @@ from ._binding import (  # noqa: F401
     build_info,
     copy_blocks,
     decode,
+    decode_noalloc,
     decode_workspace_bytes,
     last_error,
     lib,

@@ -52,6 +52,8 @@ _SIGS = {
                    _P, _SZ, _P], _I),
     "pa_decode_ex": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F, _F, _I,
                       _P, _SZ, ctypes.c_uint, _P], _I),
+    "pa_decode_noalloc": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F,
+                           _F, _I, ctypes.c_uint, _P], _I),
     "pa_prefill_chunk_workspace_bytes": ([_I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "pa_prefill_chunk": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I64,
                           _F, _I, _I, _F, _F, _P, _SZ, _P], _I),
@@ -253,6 +255,33 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int, 
             _stream(q))
     call = _issue(_lib.pa_decode_ex, args, prepared)
     return call if prepared else out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, *, block_size: int,
+                   scale: float, kv_dtype: str, max_context_len: int, k_scale: float = 1.0,
+                   v_scale: float = 1.0, out=None, shared_frames: bool = False):
+    """pa_decode_noalloc: decode with the library's own device scratch instead of a workspace
+    (for callers that cannot allocate).  Calls that overlap in time on one GPU must not be
+    issued: they share that GPU's scratch."""
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    qd = q_dtype_for(kv_dtype)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    _need_rows(block_tables, "block_tables", B, exact=False)
+    _need_rows(context_lens, "context_lens", B)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_out_like(out, q)
+    _check(_lib.pa_decode_noalloc(
+        _dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+        _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+        _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+        _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, block_size, NB,
+        float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale),
+        int(max_context_len), PA_DECODE_SHARED_FRAMES if shared_frames else 0, _stream(q)))
+    return out
 
 
 def prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,

@@ -191,6 +191,31 @@ int pa_decode_ex(void* out, const void* q, const void* k_cache, const void* v_ca
   return hip_status(pa::launch_decode(p, (hipStream_t)stream), "decode launch");
 }
 
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int max_blocks_per_seq,
+                      const int32_t* context_lens, int B, int Hq, int Hkv, int D, int block_size,
+                      int64_t NB, float scale, pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale,
+                      float v_scale, int max_context_len, unsigned flags, void* stream) {
+  // The same checks as pa_decode_ex (a null workspace of size 0 passes them only when the call
+  // needs none), then the library's own device scratch instead of a caller's workspace.
+  size_t need = 0;
+  if (B > 0 && max_context_len > 0 && D > 0 && block_size > 0 && Hq > 0)
+    need = pa::decode_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len);
+  if (need > pa::kDecodeScratchBytes)
+    return fail(PA_ENOSPC, "pa_decode_noalloc: this device needs %zu bytes of scratch, the "
+                "library holds %zu per GPU (use pa_decode with a workspace)", need,
+                pa::kDecodeScratchBytes);
+  void* scratch = nullptr;
+  if (need > 0) {
+    const hipError_t e = pa::decode_scratch(&scratch);
+    if (e != hipSuccess) return hip_status(e, "pa_decode_noalloc scratch address");
+  }
+  return pa_decode_ex(out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, B,
+                      Hq, Hkv, D, block_size, NB, scale, q_dtype, kv_dtype, k_scale, v_scale,
+                      max_context_len, scratch, need > 0 ? pa::kDecodeScratchBytes : 0, flags,
+                      stream);
+}
+
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
               int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,

@@ -42,7 +42,37 @@
 
 #include "pa_decode_impl.h"
 
+#include <mutex>
+
 namespace pa {
+
+// Device memory of the allocation-free decode entry point: a file-scope array each GPU holds
+// for the life of the process.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in); the device address of each GPU's copy comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 using namespace dec;
 

@@ -88,6 +88,12 @@ int clear_error();
 int device_compute_units();
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
+// The allocation-free decode's device scratch: kDecodeScratchBytes per GPU, in a file-scope
+// device array; decode_scratch() returns the current device's copy (its address is looked up
+// on the first call per device).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+constexpr int kMaxDevices = 64;
+hipError_t decode_scratch(void** out);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 // The decode plan (wavefront starts) of W wavefronts, computed by one workgroup.
 hipError_t launch_decode_plan(const int32_t* context_lens, int32_t* plan, int B, int Hkv, int bs,
