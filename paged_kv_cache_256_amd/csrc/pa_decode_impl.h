@@ -444,7 +444,9 @@ template <int KIND, int D>
 __device__ __forceinline__ void decode_reduce_wave(
     int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
-  constexpr int kBatch = 8;   // partials per group in flight together
+  // partials per group in flight together (8 take ~330 registers and made the merge of the
+  // 70B-shape batch 6.8 us instead of 4.6 us)
+  constexpr int kBatch = 4;
   constexpr int NV = D / 16;  // quads per lane at most (G = 16, one slice)
   const int U = plan[0];
   const int4 st = ((const int4*)(plan + 4))[k + 1];
