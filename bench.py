@@ -125,6 +125,7 @@ class DeviceState:
             self.out = torch.empty_like(self.q)
             need = pa.decode_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype, c.max_context_len)
             self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            self.groups = None
             # the caller's cache-policy hint: do several sequences' tables name the same frame?
             self.shared = c.shares_frames
         if c.chunk is not None:
@@ -197,8 +198,26 @@ class DeviceState:
                               k_scale=c.k_scale, v_scale=c.v_scale, out=self.cout,
                               workspace=self.cws, prepared=prepared)
 
+    def init_shared(self, dev):
+        """Runs of consecutive sequences that share their tables' first frames (found on the host,
+        like the block tables a scheduler hands over) for pa_decode_shared."""
+        c, pa = self.c, self.pa
+        import torch
+
+        r = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs, max(1, 16 // (c.Hq // c.Hkv)))
+        self.groups = r.to(dev)
+        need = pa.decode_shared_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype, c.max_context_len)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        return r
+
     def decode(self, prepared=False):
         c = self.c
+        if self.groups is not None:
+            return self.pa.decode_shared(self.q, self.kc, self.vc, self.tables, self.lens,
+                                         self.groups, block_size=c.bs, scale=c.scale,
+                                         kv_dtype=c.kv_dtype, max_context_len=c.max_context_len,
+                                         k_scale=c.k_scale, v_scale=c.v_scale, out=self.out,
+                                         workspace=self.ws, prepared=prepared)
         return self.pa.decode(self.q, self.kc, self.vc, self.tables, self.lens, block_size=c.bs,
                        scale=c.scale, kv_dtype=c.kv_dtype, max_context_len=c.max_context_len,
                        k_scale=c.k_scale, v_scale=c.v_scale, out=self.out, workspace=self.ws,
@@ -231,6 +250,9 @@ def main():
                          "per-tensor scales) -- the fp8 prefill-chunk variant")
     ap.add_argument("--chunk-block-size", type=int, default=None, choices=[16, 32],
                     help="config 5 only: the same mixed step with this block size")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="decode with pa_decode_shared: sequences whose tables begin with the same "
+                         "frames (config 4's branches) read them once per group")
     ap.add_argument("--long", type=int, default=None, choices=[1, 4, 16],
                     help="long-context decode instead of a named config: this many sequences of "
                          "32,768 tokens at the 70B layer shape")
@@ -267,6 +289,13 @@ def main():
         case = workloads.make(args.config)
     log(f"[bench] generated {case.name} in {time.time() - t0:.1f}s")
     st = DeviceState(case, dev)
+    groups = None
+    if args.shared_prefix:
+        if not case.B:
+            print("bench.py: --shared-prefix needs decodes", file=sys.stderr)
+            sys.exit(2)
+        groups = st.init_shared(dev)
+        log(f"[bench] {groups.num_runs} runs of sequences that share their first frames")
     torch.cuda.synchronize()
     log(f"[bench] caches filled on the GPU ({case.NB} frames)")
 
@@ -354,10 +383,14 @@ def main():
     traffic = measured_traffic(case.name) if case.B else None
     kernels = ("decode_stream_kernel + decode_reduce_kernel" if case.B <= 1024 else
                "decode_plan_kernel + decode_stream_kernel + decode_reduce_kernel")
+    if groups is not None:
+        kernels = kernels + " (runs of sequences that share frames)"
+        traffic = None
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic[0] if traffic else None,
-                "kernel": f"{kernels} (one pa_decode call, timed with HIP events)",
+                "kernel": f"{kernels} (one {'pa_decode_shared' if groups is not None else 'pa_decode'} "
+                          "call, timed with HIP events)",
                 "avg_us": round(dec_avg * 1e3, 2),
                 "algorithmic_bytes_per_launch": kv_bytes,
                 "traffic_source": traffic[1] if traffic else None}
@@ -367,10 +400,19 @@ def main():
                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
              "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None,
              "launch": "hip graph per phase" if args.graph else "eager, arguments marshalled once",
-             "attention_calls": "pa_mixed_attention" if args.mixed else
+             "attention_calls": "pa_decode_shared" if groups is not None else
+                                "pa_mixed_attention" if args.mixed else
                                 "pa_prefill_chunk + pa_decode" if case.chunk is not None and case.B else
                                 "pa_prefill_chunk" if case.chunk is not None else "pa_decode",
              "decode_shared_frames_hint": bool(case.B and st.shared)}
+    if case.B and case.shares_frames:
+        # frames several sequences reference are one copy in HBM: the bytes a decode that reads
+        # each referenced frame once must move
+        nblk = -(-case.context_lens.astype(np.int64) // case.bs)
+        used = np.unique(np.concatenate([case.block_tables[b, :nblk[b]] for b in range(case.B)]))
+        eb = {"f32": 4, "bf16": 2, "fp8": 1}[case.kv_dtype]
+        extra["kv_unique_bytes_per_step"] = int(len(used)) * 2 * case.Hkv * case.bs * case.D * eb
+        extra["kv_unique_gbs_decode"] = round(extra["kv_unique_bytes_per_step"] / (dec_avg * 1e-3) / 1e9, 1)
     if args.mixed:
         fl = chunk_flops(case)
         mavg = float(chunk_ms.mean())

@@ -190,6 +190,53 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
                       int64_t NB, float scale, pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale,
                       float v_scale, int max_context_len, unsigned flags, void* stream);
 
+/*
+ * pa_decode_shared -- pa_decode for a batch in which runs of consecutive sequences share the
+ * first frames of their block tables: the branches of one prompt in parallel sampling or beam
+ * search, which reference the prompt's frames instead of copying them (bicarait.com,
+ * "Architectural Blueprint 2" and "Physical Memory Sharing"; infoisland, section 2).  The result
+ * is pa_decode's (to fp32 rounding); the shared frames are read once per run instead of once per
+ * sequence.  A run's members put their G query heads side by side in the 16 columns of the
+ * matrix-core score tile (at G = 8 a plain decode leaves half of them empty): the run streams
+ * the shared frames once for all members, then each member's own frames with the other members'
+ * columns masked, with one online softmax per column.
+ *   Arguments shared with pa_decode have its meaning, except the workspace: at least
+ *   pa_decode_shared_workspace_bytes(...) bytes (the launch runs more wavefronts than
+ *   pa_decode's), 256-byte aligned.
+ *   run_size       int32 [B], device: run_size[b] = s >= 1 starts a run of the sequences
+ *                  [b, b + s); 0 marks a sequence inside a run.  Every sequence is in one run;
+ *                  s * G <= 16 (G = Hq / Hkv).
+ *   shared_blocks  int32 [B], device: the block-table entries the members of b's run share (the
+ *                  same for all members; 0 for a run of one).  The members' first
+ *                  shared_blocks[b] entries are equal, and shared_blocks[b] * block_size <
+ *                  context_lens[b] (the frame of the token written this step is never shared).
+ * Runs of one sequence with no shared block make this pa_decode_ex with PA_DECODE_SHARED_FRAMES.
+ * The run arrays are trusted on the device (invalid ones give unspecified results, never an
+ * access outside the buffers); check them with pa_validate_shared_prefixes on host copies.
+ */
+size_t pa_decode_shared_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype kv_dtype,
+                                        int max_context_len);
+int pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                     int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                     int max_context_len, const int32_t* shared_blocks, const int32_t* run_size,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_find_shared_prefixes -- host-only: runs for pa_decode_shared, found in host copies of a
+ * batch's block tables and context lengths.  From each sequence on, the longest stretch of at most
+ * max_run (1 .. 16; 16 / G for pa_decode_shared) consecutive sequences whose tables agree on at
+ * least their first entry becomes a run; its shared blocks are the leading entries all members
+ * agree on, limited to the blocks before each member's last token.  Sequences that join no such
+ * stretch are runs of one.  Outputs: shared_blocks and run_size (int32 [B] each), and
+ * *num_runs, the runs of two or more.  A block manager knows the same from its reference counts;
+ * this scan is for callers without one.
+ */
+int pa_find_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens, int B, int block_size, int max_run,
+                            int32_t* shared_blocks, int32_t* run_size, int* num_runs);
+
 /* Bytes of device workspace pa_prefill_chunk needs for these bounds (0 is a valid answer:
  * then workspace may be NULL).  The arguments are the ones pa_prefill_chunk receives. */
 size_t pa_prefill_chunk_workspace_bytes(int num_chunks, int64_t total_q, int max_chunk_len,
@@ -320,6 +367,13 @@ int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_se
                               const int32_t* query_start_loc, const int32_t* context_lens,
                               int num_decodes, int num_chunks, int block_size, int64_t NB,
                               int max_chunk_len, int max_context_len);
+/*  pa_validate_shared_prefixes: run_size and shared_blocks cut the batch into runs as
+ *    pa_decode_shared requires (every sequence in one run of at most 16 / G sequences, equal
+ *    shared blocks within a run, 0 for runs of one, equal shared table entries, context lengths
+ *    above the shared blocks' tokens). */
+int pa_validate_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int B, int block_size,
+                                const int32_t* shared_blocks, const int32_t* run_size, int G);
 
 /*
  * Host-side block manager (no GPU involved): the bookkeeping that produces the block tables,

@@ -7,6 +7,7 @@ declared in include/pa.h:
     copy_blocks        duplicate frames for copy-on-write
     decode             paged GQA decode attention (split over the context + reduce)
     decode_noalloc     the same decode on the library's own device scratch (allocates nothing)
+    decode_shared      decode reading a run's shared prompt frames once for all its members
     prefill_chunk      causal attention of prefill chunks over their paged context
     mixed_attention    decodes and prefill chunks of one step in one persistent kernel
     BlockManager       host-side frames, block tables, slots and copy-on-write pairs
@@ -22,7 +23,11 @@ from ._binding import (  # noqa: F401
     copy_blocks,
     decode,
     decode_noalloc,
+    decode_shared,
+    decode_shared_workspace_bytes,
     decode_workspace_bytes,
+    find_shared_prefixes,
+    SharedRuns,
     last_error,
     lib,
     mixed_attention,
@@ -37,5 +42,6 @@ from ._binding import (  # noqa: F401
     validate_copy_pairs,
     validate_decode_indices,
     validate_mixed_indices,
+    validate_shared_prefixes,
     validate_slots,
 )

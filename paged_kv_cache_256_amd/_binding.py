@@ -54,6 +54,11 @@ _SIGS = {
                       _P, _SZ, ctypes.c_uint, _P], _I),
     "pa_decode_noalloc": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F,
                            _F, _I, ctypes.c_uint, _P], _I),
+    "pa_decode_shared_workspace_bytes": ([_I, _I, _I, _I, _I, _I], _SZ),
+    "pa_decode_shared": ([_P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I64, _F, _I, _I, _F, _F,
+                          _I, _P, _P, _P, _SZ, _P], _I),
+    "pa_find_shared_prefixes": ([_P, _I, _P, _I, _I, _I, _P, _P, _P], _I),
+    "pa_validate_shared_prefixes": ([_P, _I, _P, _I, _I, _P, _P, _I], _I),
     "pa_prefill_chunk_workspace_bytes": ([_I, _I64, _I, _I, _I, _I, _I, _I, _I], _SZ),
     "pa_prefill_chunk": ([_P, _P, _P, _P, _P, _I, _P, _P, _I, _I64, _I, _I, _I, _I, _I, _I, _I64,
                           _F, _I, _I, _F, _F, _P, _SZ, _P], _I),
@@ -282,6 +287,95 @@ def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, *, block_siz
         float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale),
         int(max_context_len), PA_DECODE_SHARED_FRAMES if shared_frames else 0, _stream(q)))
     return out
+
+
+class SharedRuns:
+    """Runs of consecutive sequences that share the first frames of their block tables
+    (pa_decode_shared): run_size[b] >= 1 starts a run of run_size[b] sequences, 0 marks a
+    sequence inside a run; shared_blocks[b] is the table entries b's run shares.  int32 numpy
+    arrays (host), or tensors on the decode's device after .to(device)."""
+
+    def __init__(self, shared_blocks, run_size, num_runs: int = 0):
+        self.shared_blocks = shared_blocks
+        self.run_size = run_size
+        self.num_runs = int(num_runs)
+
+    def to(self, device):
+        def dv(a):
+            return (a if isinstance(a, torch.Tensor) else torch.from_numpy(np.ascontiguousarray(a))).to(device)
+        return SharedRuns(dv(self.shared_blocks), dv(self.run_size), self.num_runs)
+
+
+def find_shared_prefixes(block_tables, context_lens, block_size: int, max_run: int) -> SharedRuns:
+    """pa_find_shared_prefixes on host arrays: the runs of a batch (host numpy arrays)."""
+    bt, pbt = _host(block_tables, np.int32)
+    cl, pcl = _host(context_lens, np.int32)
+    B = cl.shape[0]
+    sb = np.zeros(max(B, 1), np.int32)
+    rs = np.zeros(max(B, 1), np.int32)
+    nr = ctypes.c_int(0)
+    _check(_lib.pa_find_shared_prefixes(pbt, bt.shape[1], pcl, B, int(block_size), int(max_run),
+                                        ctypes.c_void_p(sb.ctypes.data),
+                                        ctypes.c_void_p(rs.ctypes.data), ctypes.byref(nr)))
+    return SharedRuns(sb[:B].copy(), rs[:B].copy(), nr.value)
+
+
+def validate_shared_prefixes(block_tables, context_lens, block_size: int, runs: SharedRuns,
+                             G: int):
+    bt, pbt = _host(block_tables, np.int32)
+    cl, pcl = _host(context_lens, np.int32)
+    sb, psb = _host(np.asarray(runs.shared_blocks.cpu() if isinstance(runs.shared_blocks, torch.Tensor)
+                               else runs.shared_blocks), np.int32)
+    rs, prs = _host(np.asarray(runs.run_size.cpu() if isinstance(runs.run_size, torch.Tensor)
+                               else runs.run_size), np.int32)
+    if sb.shape[0] != cl.shape[0] or rs.shape[0] != cl.shape[0]:
+        raise ValueError("shared_blocks and run_size need one entry per sequence")
+    _check(_lib.pa_validate_shared_prefixes(pbt, bt.shape[1], pcl, cl.shape[0], int(block_size),
+                                            psb, prs, int(G)))
+
+
+def decode_shared_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len) -> int:
+    return int(_lib.pa_decode_shared_workspace_bytes(B, Hq, D, block_size, DTYPE_CODE[kv_dtype],
+                                                     max_context_len))
+
+
+def decode_shared(q, k_cache, v_cache, block_tables, context_lens, runs: SharedRuns, *,
+                  block_size: int, scale: float, kv_dtype: str, max_context_len: int,
+                  k_scale: float = 1.0, v_scale: float = 1.0, out=None, workspace=None,
+                  prepared: bool = False):
+    """pa_decode_shared: decode with each run's shared frames read once for all its members (runs:
+    a SharedRuns whose arrays are on q's device)."""
+    _need_outputs(prepared, out=out, workspace=workspace)
+    NB, Hkv, D = _cache_geometry(k_cache, v_cache, block_size, kv_dtype)
+    qd = q_dtype_for(kv_dtype)
+    B, Hq, Dq = q.shape
+    if Dq != D:
+        raise ValueError(f"q head_dim {Dq} != cache head_dim {D}")
+    _need_rows(block_tables, "block_tables", B, exact=False)
+    _need_rows(context_lens, "context_lens", B)
+    _need_rows(runs.shared_blocks, "shared_blocks", B)
+    _need_rows(runs.run_size, "run_size", B)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_out_like(out, q)
+    need = decode_shared_workspace_bytes(B, Hq, D, block_size, kv_dtype, max_context_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if os.environ.get("PA_VALIDATE") == "1":
+        validate_shared_prefixes(block_tables.cpu().numpy(), context_lens.cpu().numpy(),
+                                 block_size, runs, Hq // Hkv)
+    args = (_dev(out, "out", TORCH_DTYPE[qd], 3), _dev(q, "q", TORCH_DTYPE[qd], 3),
+            _dev(k_cache, "k_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(v_cache, "v_cache", TORCH_DTYPE[kv_dtype]),
+            _dev(block_tables, "block_tables", torch.int32, 2), block_tables.shape[1],
+            _dev(context_lens, "context_lens", torch.int32, 1), B, Hq, Hkv, D, block_size, NB,
+            float(scale), DTYPE_CODE[qd], DTYPE_CODE[kv_dtype], float(k_scale), float(v_scale),
+            int(max_context_len), _dev(runs.shared_blocks, "shared_blocks", torch.int32, 1),
+            _dev(runs.run_size, "run_size", torch.int32, 1), ws, wsb, _stream(q))
+    call = _issue(_lib.pa_decode_shared, args, prepared)
+    return call if prepared else out
 
 
 def prefill_chunk_workspace_bytes(num_chunks, total_q, max_chunk_len, max_context_len, Hq, Hkv,

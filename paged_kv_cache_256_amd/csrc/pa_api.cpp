@@ -9,7 +9,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <algorithm>
 #include <unordered_set>
+#include <vector>
 
 #include "pa.h"
 #include "pa_internal.h"
@@ -214,6 +216,41 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
                       Hq, Hkv, D, block_size, NB, scale, q_dtype, kv_dtype, k_scale, v_scale,
                       max_context_len, scratch, need > 0 ? pa::kDecodeScratchBytes : 0, flags,
                       stream);
+}
+
+size_t pa_decode_shared_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype kv_dtype,
+                                        int max_context_len) {
+  if (B <= 0 || Hq <= 0 || D <= 0 || block_size <= 0 || max_context_len <= 0) return 0;
+  return pa::decode_shared_workspace_bytes(D);
+}
+
+int pa_decode_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                     int B, int Hq, int Hkv, int D, int block_size, int64_t NB, float scale,
+                     pa_dtype q_dtype, pa_dtype kv_dtype, float k_scale, float v_scale,
+                     int max_context_len, const int32_t* shared_blocks, const int32_t* run_size,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || NB < 1 || max_blocks_per_seq < 1)
+    return fail(PA_EINVAL, "bad sizes (B %d, NB %lld, max_blocks_per_seq %d)", B, (long long)NB, max_blocks_per_seq);
+  if (B > 65535) return fail(PA_ENOTSUP, "batch %d too large for one call (max 65535)", B);
+  if (int r = check_heads(Hq, Hkv)) return r;
+  if (int r = check_shape(D, block_size, kv_dtype)) return r;
+  if (int r = check_attn_dtypes(q_dtype, kv_dtype)) return r;
+  if (int r = check_scales(kv_dtype, k_scale, v_scale)) return r;
+  if (!std::isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (B == 0) return ok();
+  if (max_context_len < 1) return fail(PA_EINVAL, "max_context_len %d must be positive", max_context_len);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !shared_blocks || !run_size)
+    return fail(PA_EINVAL, "null pointer argument");
+  const size_t need = pa::decode_shared_workspace_bytes(D);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PA_ENOSPC, "workspace of %zu bytes needed, %zu given", need, workspace ? workspace_bytes : (size_t)0);
+  if (need > 0 && ((uintptr_t)workspace & 255u))
+    return fail(PA_EINVAL, "workspace must be 256-byte aligned");
+  pa::DecodeParams p{out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                     B, Hq, Hkv, D, block_size, NB, scale, (int)kv_dtype, k_scale, v_scale,
+                     max_context_len, need > 0 ? workspace : nullptr, true, run_size, shared_blocks};
+  return hip_status(pa::launch_decode(p, (hipStream_t)stream), "decode_shared launch");
 }
 
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -496,6 +533,82 @@ int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_se
   return check_chunks(block_tables, max_blocks_per_seq, query_start_loc, context_lens,
                       num_decodes, num_chunks, num_decodes, block_size, NB, max_chunk_len,
                       max_context_len);
+}
+
+int pa_find_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,
+                            const int32_t* context_lens, int B, int block_size, int max_run,
+                            int32_t* shared_blocks, int32_t* run_size, int* num_runs) {
+  if (B < 0 || max_blocks_per_seq < 1 || block_size < 1 || max_run < 1 || max_run > 16)
+    return fail(PA_EINVAL, "bad sizes (B %d, max_blocks_per_seq %d, block_size %d, max_run %d)",
+                B, max_blocks_per_seq, block_size, max_run);
+  if (!num_runs || (B > 0 && (!block_tables || !context_lens || !shared_blocks || !run_size)))
+    return fail(PA_EINVAL, "null pointer argument");
+  // full blocks before the token at position L - 1 (the one a decode step has just written)
+  auto full = [&](int b) {
+    const int L = context_lens[b];
+    return L >= 1 ? std::min((L - 1) / block_size, max_blocks_per_seq) : 0;
+  };
+  auto row = [&](int b) { return block_tables + (size_t)b * max_blocks_per_seq; };
+  int runs = 0;
+  for (int b = 0; b < B;) {
+    // the longest stretch from b of at most max_run sequences that share at least one full block
+    int e = b + 1, P = full(b);
+    while (e < B && e - b < max_run && P >= 1) {
+      int f = 0;
+      const int lim = std::min(P, full(e));
+      while (f < lim && row(e)[f] == row(b)[f]) ++f;
+      if (f < 1) break;
+      P = f;
+      ++e;
+    }
+    if (e - b >= 2 && P >= 1 && row(b)[0] >= 0) {
+      for (int m = b; m < e; ++m) {
+        shared_blocks[m] = P;
+        run_size[m] = m == b ? e - b : 0;
+      }
+      ++runs;
+    } else {
+      e = b + 1;
+      shared_blocks[b] = 0;
+      run_size[b] = 1;
+    }
+    b = e;
+  }
+  *num_runs = runs;
+  return ok();
+}
+
+int pa_validate_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,
+                                const int32_t* context_lens, int B, int block_size,
+                                const int32_t* shared_blocks, const int32_t* run_size, int G) {
+  if (B < 0 || max_blocks_per_seq < 1 || block_size < 1 || G < 1 || G > 16)
+    return fail(PA_EINVAL, "bad sizes");
+  if (B == 0) return ok();
+  if (!block_tables || !context_lens || !shared_blocks || !run_size)
+    return fail(PA_EINVAL, "null pointer argument");
+  for (int b = 0; b < B;) {
+    const int s = run_size[b];
+    if (s < 1) return fail(PA_EINVAL, "run_size[%d] = %d: sequence %d starts no run and is in none", b, s, b);
+    if (b + s > B) return fail(PA_ERANGE, "run at %d of %d sequences runs past the batch", b, s);
+    if (s * G > 16)
+      return fail(PA_ERANGE, "run at %d has %d sequences: %d x %d query heads exceed 16 columns", b, s, s, G);
+    const int P = shared_blocks[b];
+    if (s == 1 && P != 0) return fail(PA_EINVAL, "shared_blocks[%d] = %d for a run of one", b, P);
+    if (P < 0 || P > max_blocks_per_seq) return fail(PA_ERANGE, "shared_blocks[%d] = %d", b, P);
+    for (int m = b; m < b + s; ++m) {
+      if (m > b && run_size[m] != 0)
+        return fail(PA_EINVAL, "run_size[%d] = %d inside the run that starts at %d", m, run_size[m], b);
+      if (shared_blocks[m] != P)
+        return fail(PA_EINVAL, "shared_blocks[%d] = %d differs from its run's %d", m, shared_blocks[m], P);
+      if ((long long)P * block_size >= context_lens[m])
+        return fail(PA_EINVAL, "sequence %d: %d shared blocks leave no frame of its own among its %d tokens", m, P, context_lens[m]);
+      for (int f = 0; f < P; ++f)
+        if (block_tables[(size_t)m * max_blocks_per_seq + f] != block_tables[(size_t)b * max_blocks_per_seq + f])
+          return fail(PA_EINVAL, "block_tables[%d][%d] differs from the shared frame of its run", m, f);
+    }
+    b += s;
+  }
+  return ok();
 }
 
 }  // extern "C"

@@ -40,6 +40,8 @@
 // output.
 
 
+#include <algorithm>
+
 #include "pa_decode_impl.h"
 
 #include <mutex>
@@ -86,14 +88,20 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 // offsets (in LDS) and a walk over at most `per` sequences, one thread per wavefront.
 __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __restrict__ context_lens,
                                                            int32_t* __restrict__ plan, int B,
-                                                           int Hkv, int BS, int cap, int W) {
+                                                           int Hkv, int BS, int cap, int W,
+                                                           Runs runs) {
+  // (runs.size null: every sequence is a run of its own)
+  auto units_of = [&](int b) {
+    return run_units(runs.size ? run_frames<true>(context_lens, b, B, cap, BS, runs)
+                               : run_frames<false>(context_lens, b, B, cap, BS, runs));
+  };
   __shared__ int32_t wsum[16];
   __shared__ int32_t tex[1024];  // units before thread t's first sequence
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int per = (B + 1023) / 1024;
   const int b0 = min(B, t * per), b1 = min(B, b0 + per);
   int mine = 0;
-  for (int b = b0; b < b1; ++b) mine += run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
+  for (int b = b0; b < b1; ++b) mine += units_of(b);
   int incl = mine;
   for (int off = 1; off < 64; off <<= 1) {
     const int v = __shfl_up(incl, off);
@@ -126,7 +134,7 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
     const int bend = min(B, b + per);
     int su = 0;
     for (; b < bend; ++b) {
-      su = run_units((max(0, min(context_lens[b], cap)) + BS - 1) / BS);
+      su = units_of(b);
       if (ap < cc + su) break;
       cc += su;
     }
@@ -140,31 +148,34 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
   }
 }
 
-template <int KIND, int D, int BS, int F, bool NT>
-__global__ __launch_bounds__(kWaves * 64, kWgPerCu) void decode_stream_kernel(
+// (GROUPED runs hold more per lane -- the members' columns, their chunk bounds -- and take up to
+// 512 registers: the launch of 3 wavefronts per CU has at most one workgroup on a CU anyway)
+template <int KIND, int D, int BS, int F, bool NT, bool GROUPED>
+__global__ __launch_bounds__(kWaves * 64, GROUPED ? 1 : kWgPerCu) void decode_stream_kernel(
     void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
-    long long NB, int cap, float qk_scale, float v_scale) {
+    long long NB, int cap, float qk_scale, float v_scale, Runs runs) {
   // Workgroups reach the 8 XCDs round-robin by id.  XCD k (workgroups k, k + 8, ...) takes the
   // k-th eighth of the ranges, so that runs next to each other in the batch -- branches that share
   // frames -- stream through the same L2.
   const int nwg = gridDim.x;
   const int r = nwg % kXcds == 0 ? (blockIdx.x % kXcds) * (nwg / kXcds) + blockIdx.x / kXcds
                                  : blockIdx.x;
-  decode_stream_wave<KIND, D, BS, F, NT>(
+  decode_stream_wave<KIND, D, BS, F, NT, GROUPED>(
       r * kWaves + uniform(threadIdx.x >> 6), gridDim.x * kWaves, out, q, k_cache,
       v_cache, block_tables, context_lens, plan, inline_plan, ws_ml, ws_o, B, mbps, Hq, Hkv, G,
-      NB, cap, qk_scale, v_scale);
+      NB, cap, qk_scale, v_scale, runs);
 }
 
-template <int KIND, int D>
+template <int KIND, int D, bool GROUPED>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
-  decode_reduce_wave<KIND, D>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq, Hkv, G, W,
-                              v_scale);
+    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale, Runs runs,
+    int B) {
+  decode_reduce_wave<KIND, D, GROUPED>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq, Hkv,
+                                       G, W, v_scale, runs, B);
 }
 
 // Wavefronts of a launch: the full stream (3 per CU) unless the batch holds too few units for it.
@@ -184,12 +195,24 @@ inline int launch_waves(int B, int Hkv, int cap, int BS) {
   return w >= full ? full : (int)(w > kWaves ? w : kWaves);
 }
 
+// Runs of sequences that share frames (pa_decode_shared) launch 4 wavefronts per CU, one per
+// SIMD with up to 512 registers each: measured on the 70B-shape fp8 copy-on-write batch (128 runs
+// of two branches), 93.4 us against 104.5 us at 3 per CU; two more frames per pipeline step
+// instead made it 117 us.  The L2 / MALL hits on the shared frames leave that stream short of
+// loads in flight rather than of HBM bandwidth, and the extra wavefronts add them.
+constexpr int kGroupedWavesPerCu = 4;
+
+inline int grouped_waves() { return device_compute_units() * kGroupedWavesPerCu / kWaves * kWaves; }
+
 template <int KIND, int D, int BS>
 hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   constexpr int F = step_frames<KIND, D, BS>();
   const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
                                                                  : p.max_blocks_per_seq * BS;
-  const Layout l = layout(D, launch_waves(p.B, p.Hkv, cap, BS));  // within the workspace's size
+  const int Ws = launch_waves(p.B, p.Hkv, cap, BS);
+  const Layout l = layout(D, p.run_size ? std::min(Ws / kStreamWavesPerCu * kGroupedWavesPerCu,
+                                                   grouped_waves())
+                                        : Ws);  // within the workspace's size
   int32_t* plan = (int32_t*)p.workspace;
   float* ws_ml = (float*)((char*)p.workspace + l.plan_bytes);
   float* ws_o = (float*)((char*)p.workspace + l.plan_bytes + l.ml_bytes);
@@ -197,22 +220,28 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const float qk_scale = p.scale * (KIND == KFP8 ? p.k_scale : 1.0f) * kLog2e;
   const float v_scale = KIND == KFP8 ? p.v_scale : 1.0f;
   const bool inline_plan = p.B <= kInlinePlanMax;
+  const Runs runs{p.run_size, p.shared_blocks};
+  const bool grouped = p.run_size != nullptr;
   hipError_t e;
   if (!inline_plan) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p.context_lens, plan,
-                       p.B, p.Hkv, BS, cap, l.W);
+                       p.B, p.Hkv, BS, cap, l.W, runs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  auto stream_kernel = p.shared_frames ? decode_stream_kernel<KIND, D, BS, F, false>
-                                       : decode_stream_kernel<KIND, D, BS, F, true>;
+  // runs of sequences that share frames (pa_decode_shared) keep their tiles cacheable too
+  auto stream_kernel = grouped ? decode_stream_kernel<KIND, D, BS, F, false, true>
+                       : p.shared_frames ? decode_stream_kernel<KIND, D, BS, F, false, false>
+                                         : decode_stream_kernel<KIND, D, BS, F, true, false>;
   hipLaunchKernelGGL(stream_kernel, dim3(l.W / kWaves), dim3(kWaves * 64), 0, stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
                      p.block_tables, p.context_lens, plan, inline_plan, ws_ml, ws_o, p.B,
-                     p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale);
+                     p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale,
+                     runs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_reduce_kernel<KIND, D>), dim3(l.W - 1), dim3(64), 0, stream, p.out,
-                     ws_ml, ws_o, plan, p.Hq, p.Hkv, G, l.W, v_scale);
+  auto reduce_kernel = grouped ? decode_reduce_kernel<KIND, D, true> : decode_reduce_kernel<KIND, D, false>;
+  hipLaunchKernelGGL(reduce_kernel, dim3(l.W - 1), dim3(64), 0, stream, p.out, ws_ml, ws_o, plan,
+                     p.Hq, p.Hkv, G, l.W, v_scale, runs, p.B);
   return hipGetLastError();
 }
 
@@ -235,10 +264,15 @@ size_t decode_workspace_bytes(int /*B*/, int /*Hq*/, int D, int /*bs*/, int /*kv
   return l.plan_bytes + l.ml_bytes + l.o_bytes;
 }
 
+size_t decode_shared_workspace_bytes(int D) {
+  const Layout l = layout(D, grouped_waves());
+  return l.plan_bytes + l.ml_bytes + l.o_bytes;
+}
+
 hipError_t launch_decode_plan(const int32_t* context_lens, int32_t* plan, int B, int Hkv, int bs,
                               int cap, int W, hipStream_t stream) {
   hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, context_lens, plan, B, Hkv,
-                     bs, cap, W);
+                     bs, cap, W, Runs{});
   return hipGetLastError();
 }
 

@@ -70,8 +70,43 @@ struct Start {
   long long F;
 };
 
+// Runs of a batch whose sequences share the first frames of their block tables (the GROUPED
+// variant of the bodies below; branches of one prompt).  size[b] >= 1 starts a run of the
+// consecutive sequences [b, b + size[b]); size[b] = 0 marks a sequence inside a run.  The members
+// of a run share their first shared[b] block-table entries (0 for a run of one), and their G
+// query heads each take G of the 16 columns of the score tile: the run streams the shared frames
+// once for all members, then each member's own frames with the other members' columns masked.
+struct Runs {
+  const int32_t* size;
+  const int32_t* shared;
+};
+
+__host__ __device__ inline int blocks_of(const int32_t* __restrict__ context_lens, int b, int cap,
+                                         int BS) {
+  return (max(0, min(context_lens[b], cap)) + BS - 1) / BS;
+}
+
+// Frames of the run that sequence b leads: its blocks, plus every other member's blocks after the
+// shared ones (0 if b is inside another run).
+template <bool GROUPED>
+__device__ inline int run_frames(const int32_t* __restrict__ context_lens, int b, int B, int cap,
+                                 int BS, Runs runs) {
+  const int nb = blocks_of(context_lens, b, cap, BS);
+  if constexpr (!GROUPED) {
+    return nb;
+  } else {
+    const int sz = runs.size[b];
+    if (sz <= 0) return 0;
+    const int P = runs.shared[b];
+    int n = nb;
+    for (int mm = 1; mm < sz && b + mm < B; ++mm) n += blocks_of(context_lens, b + mm, cap, BS) - P;
+    return n;
+  }
+}
+
+template <bool GROUPED = false>
 __device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int B, int Hkv, int BS,
-                                  int cap, int W, int w, int lane) {
+                                  int cap, int W, int w, int lane, Runs runs = Runs{}) {
   constexpr int kPer = kInlinePlanMax / 64;
   const int per = (B + 63) / 64;
   int un[kPer];
@@ -79,8 +114,8 @@ __device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int 
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int bb = lane * per + i;
-    const int L = (i < per && bb < B) ? max(0, min(context_lens[bb], cap)) : 0;
-    un[i] = run_units((L + BS - 1) / BS);
+    un[i] = (i < per && bb < B) ? run_units(run_frames<GROUPED>(context_lens, bb, B, cap, BS, runs))
+                                : 0;
     mine += un[i];
   }
   int incl = mine;
@@ -118,14 +153,15 @@ __device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int 
 
 __device__ inline long long range_begin(long long F, int w, int W) { return F * w / W; }
 
-// The work of wavefront w out of the W wavefronts that split the batch.
-template <int KIND, int D, int BS, int F, bool NT>
+// The work of wavefront w out of the W wavefronts that split the batch.  (GROUPED: the units are
+// the runs of `runs` instead of single sequences.)
+template <int KIND, int D, int BS, int F, bool NT, bool GROUPED = false>
 __device__ __forceinline__ void decode_stream_wave(
     int w, int W, void* __restrict__ out, const void* __restrict__ q, const char* __restrict__ k_cache,
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
-    long long NB, int cap, float qk_scale, float v_scale) {
+    long long NB, int cap, float qk_scale, float v_scale, Runs runs = Runs{}) {
   using Ops = KvOps<KIND, D, BS>;
   constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
   constexpr int NGS = F * KG;  // 16-key groups per step
@@ -137,7 +173,7 @@ __device__ __forceinline__ void decode_stream_wave(
   long long Ftot;
   int b, g, u;  // u: unit within the run
   if (inline_plan) {
-    const Start st = wave_plan(context_lens, B, Hkv, BS, cap, W, w, lane);
+    const Start st = wave_plan<GROUPED>(context_lens, B, Hkv, BS, cap, W, w, lane, runs);
     Ftot = st.F;
     b = st.b;
     g = st.g;
@@ -166,6 +202,7 @@ __device__ __forceinline__ void decode_stream_wave(
   int vfid = 0, vstride = 0;
   uint64_t live_mask = 0;
   int L = 0, cblk = 0;  // context length and first block of the current chunk
+  int col0 = 0, col1 = 16;  // GROUPED: score columns (member heads) the current chunk is for
 
   // Gather step s of a chunk whose frame ids (one per lane) and lane strides are fid / fstride,
   // for kv head gg.
@@ -205,7 +242,9 @@ __device__ __forceinline__ void decode_stream_wave(
         for (int sl = 0; sl < NS; ++sl) sv = Ops::qk(sv, Ops::kop(kt[f], h, sl), Ops::qop(qw, sl));
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) {
-          const float v = (16 * h + 4 * j + ii < valid) ? sv[ii] * qk_scale : -INFINITY;
+          bool keep = 16 * h + 4 * j + ii < valid;
+          if constexpr (GROUPED) keep = keep && n >= col0 && n < col1;
+          const float v = keep ? sv[ii] * qk_scale : -INFINITY;
           sc[f * KG + h][ii] = v;
           mx = fmaxf(mx, v);
         }
@@ -223,8 +262,17 @@ __device__ __forceinline__ void decode_stream_wave(
     }
     mx = wave_max_over_j(mx);
     const float mnew = fmaxf(m, mx);
-    if (mnew == -INFINITY) return;  // nothing live yet
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    float mref = mnew;  // the exponentials' shift
+    if constexpr (GROUPED) {
+      // a member's columns may have seen no key yet while another member's are live: the step is
+      // skipped only when no column has, and a column still at -inf shifts by 0 (its
+      // probabilities are exp2(-inf) = 0 and its state stays empty)
+      if (!__builtin_amdgcn_ballot_w64(mnew != -INFINITY)) return;
+      mref = mnew == -INFINITY ? 0.f : mnew;
+    } else {
+      if (mnew == -INFINITY) return;  // nothing live yet
+    }
+    const float alpha = GROUPED && m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
     m = mnew;
     lsum *= alpha;
 #pragma unroll
@@ -234,7 +282,7 @@ __device__ __forceinline__ void decode_stream_wave(
     for (int gi = 0; gi < NGS; ++gi) {
       f32x4 p;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(sc[gi][ii] - mnew);
+      for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(sc[gi][ii] - mref);
       pf[gi] = Ops::pfrag(p, lsum);
     }
 #pragma unroll
@@ -260,6 +308,7 @@ __device__ __forceinline__ void decode_stream_wave(
   // steps of tiles in flight from its first frame to its last.
   struct Piece {
     int b, g, L, nblk, f0, n, slot;
+    int sz, P;  // GROUPED: members of the run and their shared blocks
     bool complete;
   };
   long long x = a;  // first unit of the next run to look at
@@ -268,7 +317,8 @@ __device__ __forceinline__ void decode_stream_wave(
   auto find_piece = [&](Piece& pc) -> bool {
     while (x < e && rb < B) {
       const int Lr = max(0, min(context_lens[rb], cap));
-      const int nb = (Lr + BS - 1) / BS;
+      const int nb = GROUPED ? run_frames<GROUPED>(context_lens, rb, B, cap, BS, runs)
+                             : (Lr + BS - 1) / BS;
       const int units = (int)min((long long)(run_units(nb) - ru), e - x);
       // frames of the run inside this wavefront's range (its first kRestart units hold none)
       const int f0 = max(0, ru - kRestart), f1 = min(nb, ru + units - kRestart);
@@ -289,6 +339,10 @@ __device__ __forceinline__ void decode_stream_wave(
         pc.n = f1 - f0;
         pc.complete = f0 == 0 && f1 == nb;
         pc.slot = s0 > a ? 1 : 0;
+        if constexpr (GROUPED) {
+          pc.sz = runs.size[pb];
+          pc.P = runs.shared[pb];
+        }
         return true;
       }
     }
@@ -298,10 +352,49 @@ __device__ __forceinline__ void decode_stream_wave(
   auto chunk_id = [&](const Piece& pc, int c0) {
     return block_tables[(size_t)pc.b * mbps + min(pc.f0 + c0 + lane, pc.nblk - 1)];
   };
-  // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G)
+  // GROUPED: a chunk is up to kIds frames of one table row -- the shared frames (read from the
+  // first member's row, for every member's columns) or one member's own frames (its columns).
+  struct Chunk {
+    int row, blk0, len, L, col0, col1;
+  };
+  auto chunk_of = [&](const Piece& pc, int c0) {
+    Chunk ch;
+    const int x = pc.f0 + c0;  // frame of the run
+    int end;
+    if (x < pc.P) {
+      ch.row = pc.b;
+      ch.blk0 = x;
+      end = pc.P;
+      ch.L = pc.L;
+      ch.col0 = 0;
+      ch.col1 = 16;
+    } else {
+      int cum = pc.P, mm = 0, nbm = 0;
+      for (; mm < pc.sz && pc.b + mm < B; ++mm) {
+        nbm = blocks_of(context_lens, pc.b + mm, cap, BS);
+        if (x < cum + nbm - pc.P) break;
+        cum += nbm - pc.P;
+      }
+      mm = min(mm, min(pc.sz, B - pc.b) - 1);
+      ch.row = pc.b + mm;
+      ch.blk0 = pc.P + (x - cum);
+      end = cum + nbm - pc.P;
+      ch.L = max(0, min(context_lens[pc.b + mm], cap));
+      ch.col0 = mm * G;
+      ch.col1 = (mm + 1) * G;
+    }
+    ch.len = max(1, min(kIds, min(pc.n - c0, end - x)));
+    return ch;
+  };
+  auto chunk_id_of = [&](const Chunk& ch) {
+    return block_tables[(size_t)ch.row * mbps + max(0, min(ch.blk0 + min(lane, ch.len - 1), mbps - 1))];
+  };
+  // query fragment of row n: dims (D/4)*j .. of head g*G + n (zero if n >= G); GROUPED: column n
+  // is head n % G of member n / G
   auto load_q = [&](uint32_t (&dst)[QW], const Piece& pc) {
-    const bool qv = n < G;
-    const size_t row = (size_t)pc.b * Hq + (size_t)pc.g * G + (qv ? n : 0);
+    const bool qv = GROUPED ? n < pc.sz * G && pc.b + n / G < B : n < G;
+    const size_t row = GROUPED ? (size_t)(pc.b + (qv ? n / G : 0)) * Hq + (size_t)pc.g * G + (qv ? n % G : 0)
+                               : (size_t)pc.b * Hq + (size_t)pc.g * G + (qv ? n : 0);
     const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
 #pragma unroll
     for (int i = 0; i < QW / 4; ++i) {
@@ -320,10 +413,12 @@ __device__ __forceinline__ void decode_stream_wave(
   };
   auto finalize = [&](const Piece& pc) {
     const float lrow = wave_sum_over_j(lsum);
-    if (n < G) {
+    const bool nrow = GROUPED ? n < pc.sz * G && pc.b + n / G < B : n < G;
+    if (nrow) {
       if (pc.complete) {
         const float inv = v_scale / lrow;
-        const size_t o = ((size_t)pc.b * Hq + (size_t)pc.g * G + n) * D + 4 * j;
+        const size_t o = GROUPED ? ((size_t)(pc.b + n / G) * Hq + (size_t)pc.g * G + n % G) * D + 4 * j
+                                 : ((size_t)pc.b * Hq + (size_t)pc.g * G + n) * D + 4 * j;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           if constexpr (KIND == KF32) {
@@ -350,9 +445,19 @@ __device__ __forceinline__ void decode_stream_wave(
   Piece pc;
   if (!find_piece(pc)) return;
   int c0 = 0;  // first frame of the current chunk within its piece
-  L = pc.L;
-  cblk = pc.f0;
-  resolve(chunk_id(pc, 0), min(kIds, pc.n), true, vfid, vstride, live_mask);
+  Chunk cc{}, cx{};  // GROUPED: the current and the next chunk
+  if constexpr (GROUPED) {
+    cc = chunk_of(pc, 0);
+    L = cc.L;
+    cblk = cc.blk0;
+    col0 = cc.col0;
+    col1 = cc.col1;
+    resolve(chunk_id_of(cc), cc.len, true, vfid, vstride, live_mask);
+  } else {
+    L = pc.L;
+    cblk = pc.f0;
+    resolve(chunk_id(pc, 0), min(kIds, pc.n), true, vfid, vstride, live_mask);
+  }
   load_q(qw, pc);
   m = -INFINITY;
   lsum = 0.f;
@@ -368,7 +473,7 @@ __device__ __forceinline__ void decode_stream_wave(
   for (;;) {
     // the next chunk: the rest of this piece, or the next piece
     Piece pn = pc;
-    int c0n = c0 + kIds;
+    int c0n = c0 + (GROUPED ? cc.len : kIds);
     bool more = c0n < pc.n;
     if (!more) {
       c0n = 0;
@@ -376,10 +481,17 @@ __device__ __forceinline__ void decode_stream_wave(
     }
     // its raw ids and query, fetched now and used at the end of this chunk
     int f_raw_n = 0;
-    if (more) f_raw_n = chunk_id(pn, c0n);
+    if constexpr (GROUPED) {
+      if (more) {
+        cx = chunk_of(pn, c0n);
+        f_raw_n = chunk_id_of(cx);
+      }
+    } else {
+      if (more) f_raw_n = chunk_id(pn, c0n);
+    }
     if constexpr (kPrefetchQ) load_q(qn, pn);
-    const int cnn = more ? min(kIds, pn.n - c0n) : 0;
-    const int cn = min(kIds, pc.n - c0);
+    const int cnn = more ? (GROUPED ? cx.len : min(kIds, pn.n - c0n)) : 0;
+    const int cn = GROUPED ? cc.len : min(kIds, pc.n - c0);
     const int np = (cn + 2 * F - 1) / (2 * F) * 2;  // steps of the chunk, an even count
     int vfid_n = 0, vstride_n = 0;
     uint64_t live_n = 0;
@@ -396,13 +508,21 @@ __device__ __forceinline__ void decode_stream_wave(
       compute_step(kB, vB, s + 1);
       load_next(kB, vB, s + 3);
     }
-    if (c0 + kIds >= pc.n) finalize(pc);
+    if (c0 + cn >= pc.n) finalize(pc);
     if (!more) break;
     const bool fresh = c0n == 0;
     pc = pn;
     c0 = c0n;
-    L = pc.L;
-    cblk = pc.f0 + c0;
+    if constexpr (GROUPED) {
+      cc = cx;
+      L = cc.L;
+      cblk = cc.blk0;
+      col0 = cc.col0;
+      col1 = cc.col1;
+    } else {
+      L = pc.L;
+      cblk = pc.f0 + c0;
+    }
     vfid = vfid_n;
     vstride = vstride_n;
     live_mask = live_n;
@@ -439,11 +559,13 @@ __device__ __forceinline__ void decode_stream_wave(
 // columns per lane); the 64 / LPG groups of the wavefront take the partials in turn (partial p by
 // group p mod groups), each with its own running (max, sum, accumulator), and the groups are
 // combined by the same rule with lane swaps at the end.  The merge order depends only on the
-// sizes, so equal inputs give equal bits.
-template <int KIND, int D>
+// sizes, so equal inputs give equal bits.  (GROUPED: a run's rows are its members' heads, row r
+// being head r % G of member r / G.)
+template <int KIND, int D, bool GROUPED = false>
 __device__ __forceinline__ void decode_reduce_wave(
     int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
-    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale) {
+    const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale,
+    Runs runs = Runs{}, int B = 0) {
   // partials per group in flight together (8 take ~330 registers and made the merge of the
   // 70B-shape batch 6.8 us instead of 4.6 us)
   constexpr int kBatch = 4;
@@ -465,10 +587,16 @@ __device__ __forceinline__ void decode_reduce_wave(
   const int sl = k - w0;  // this wavefront's slice
   if (sl >= S) return;
   const int b = st.x, g = st.y;
+  // rows of the run, and a power of two at least that many for the lane layout
+  const int rows = GROUPED ? min(runs.size[b] * G, min(16, (B - b) * G)) : G;
+  int Gr = G;
+  if constexpr (GROUPED) {
+    while (Gr < rows) Gr *= 2;
+  }
   const int cq = D / (4 * S);                  // quads of a slice row
-  const int lpr = cq < 64 / G ? cq : 64 / G;   // lanes per row in a group
+  const int lpr = cq < 64 / Gr ? cq : 64 / Gr; // lanes per row in a group
   const int qpl = cq / lpr;                    // quads per lane
-  const int lpg = G * lpr;                     // lanes per group
+  const int lpg = Gr * lpr;                    // lanes per group
   const int groups = 64 / lpg;
   const int grp = lane / lpg, rr = (lane % lpg) / lpr, ql = lane % lpr;
   const int col = sl * (D / S) + ql * qpl * 4;  // first output column of the lane
@@ -486,6 +614,7 @@ __device__ __forceinline__ void decode_reduce_wave(
       const int w = wb + i * groups;
       bool has = w <= w1;
       if (!dense && has) has = F * w / W < F * (w + 1) / W;
+      if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
       const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
       const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
       const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
@@ -528,8 +657,10 @@ __device__ __forceinline__ void decode_reduce_wave(
     M = Mn;
   }
   if (grp != 0) return;
+  if (GROUPED && rr >= rows) return;
   const float inv = v_scale / den;
-  const size_t o = ((size_t)b * Hq + (size_t)g * G + rr) * D + col;
+  const size_t o = GROUPED ? ((size_t)(b + rr / G) * Hq + (size_t)g * G + rr % G) * D + col
+                           : ((size_t)b * Hq + (size_t)g * G + rr) * D + col;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     if (v >= qpl) break;

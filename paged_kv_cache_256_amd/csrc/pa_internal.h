@@ -27,6 +27,11 @@ struct DecodeParams {
   int max_context_len;
   void* workspace;
   bool shared_frames;  // frames referenced by several sequences: keep them cacheable
+  // runs of consecutive sequences that share their first block-table entries (pa_decode_shared;
+  // null for pa_decode): run_size[b] >= 1 starts a run of run_size[b] sequences, 0 marks a
+  // sequence inside one; shared_blocks[b] is the shared entries of b's run
+  const int32_t* run_size = nullptr;
+  const int32_t* shared_blocks = nullptr;
 };
 
 struct PrefillParams {
@@ -88,6 +93,8 @@ int clear_error();
 int device_compute_units();
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
+// Workspace of a decode over runs of sequences that share frames (more wavefronts per CU).
+size_t decode_shared_workspace_bytes(int D);
 // The allocation-free decode's device scratch: kDecodeScratchBytes per GPU, in a file-scope
 // device array; decode_scratch() returns the current device's copy (its address is looked up
 // on the first call per device).

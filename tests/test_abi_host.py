@@ -443,3 +443,59 @@ def test_binding_rejects_index_tensors_of_the_wrong_size():
 def test_validate_mixed_indices_of_an_empty_batch_reads_nothing():
     f = lib().pa_validate_mixed_indices
     assert f(NULL, 1, NULL, NULL, 0, 0, 16, 8, 1, 16) == OK
+
+
+def test_find_shared_prefixes_makes_runs_of_consecutive_sequences():
+    bs = 16
+    tables = np.array([
+        [5, 6, 7, 40, -1],     # 0: run A (frames 5, 6 shared with 1 and 2)
+        [5, 6, 8, -1, -1],     # 1: run A
+        [5, 6, 7, 41, 42],     # 2: run A
+        [9, 1, 2, 3, -1],      # 3: run B with 4
+        [9, 1, 2, 3, 4],       # 4: run B: shares 9, 1, 2 (3's last token is in block 3)
+        [11, -1, -1, -1, -1],  # 5: one block holding its last token: no full block, alone
+        [5, 6, 7, 7, -1],      # 6: first frame 5 again, but not next to run A: alone
+    ], np.int32)
+    lens = np.array([60, 40, 70, 64, 80, 10, 50], np.int32)
+    r = pa.find_shared_prefixes(tables, lens, bs, 8)
+    assert r.run_size.tolist() == [3, 0, 0, 2, 0, 1, 1]
+    assert r.shared_blocks.tolist() == [2, 2, 2, 3, 3, 0, 0]
+    assert r.num_runs == 2
+    pa.validate_shared_prefixes(tables, lens, bs, r, 4)
+    # runs of at most two: A splits into [0, 1] and [2] (alone)
+    r2 = pa.find_shared_prefixes(tables, lens, bs, 2)
+    assert r2.run_size.tolist() == [2, 0, 1, 2, 0, 1, 1]
+    assert r2.shared_blocks.tolist() == [2, 2, 0, 3, 3, 0, 0]
+    pa.validate_shared_prefixes(tables, lens, bs, r2, 8)
+    with pytest.raises(pa.PAError, match="exceed 16 columns"):
+        pa.validate_shared_prefixes(tables, lens, bs, r, 8)  # a run of 3 at G = 8
+
+
+def test_validate_shared_prefixes_rejects_inconsistent_runs():
+    bs = 16
+    tables = np.array([[5, 6, 7], [5, 6, 8], [5, 9, 1]], np.int32)
+    lens = np.array([40, 40, 40], np.int32)
+    ok = pa.SharedRuns(np.array([2, 2, 0], np.int32), np.array([2, 0, 1], np.int32))
+    pa.validate_shared_prefixes(tables, lens, bs, ok, 8)
+    bad = [
+        (pa.SharedRuns(np.array([2, 2, 2], np.int32), np.array([3, 0, 0], np.int32)), "differs from the shared frame"),
+        (pa.SharedRuns(np.array([2, 2, 1], np.int32), np.array([2, 0, 1], np.int32)), "for a run of one"),
+        (pa.SharedRuns(np.array([3, 3, 0], np.int32), np.array([2, 0, 1], np.int32)), "leave no frame"),
+        (pa.SharedRuns(np.array([2, 2, 0], np.int32), np.array([2, 1, 1], np.int32)), "inside the run"),
+        (pa.SharedRuns(np.array([2, 2, 0], np.int32), np.array([2, 0, 0], np.int32)), "starts no run"),
+        (pa.SharedRuns(np.array([2, 1, 0], np.int32), np.array([2, 0, 1], np.int32)), "differs from its run"),
+        (pa.SharedRuns(np.array([0, 0, 0], np.int32), np.array([1, 1, 2], np.int32)), "past the batch"),
+    ]
+    for runs, msg in bad:
+        with pytest.raises(pa.PAError, match=msg):
+            pa.validate_shared_prefixes(tables, lens, bs, runs, 4)
+
+
+def test_decode_shared_checks_its_arguments():
+    f = lib().pa_decode_shared
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 4, 64, 8, 128, 32, 64, 0.1, BF16, FP8, 1.0, 1.0,
+            1024]
+    need = lib().pa_decode_workspace_bytes(4, 64, 128, 32, FP8, 1024)
+    assert f(*base, NULL, FAKE, FAKE, need, NULL) == EINVAL and "null" in err()
+    assert f(*base, FAKE, FAKE, FAKE, need - 1, NULL) == ENOSPC
+    assert f(*base[:18], 0, FAKE, FAKE, FAKE, need, NULL) == EINVAL  # max_context_len 0

@@ -347,6 +347,7 @@ def fork_case(name: str, seed: int, *, prompts: int = 32, branches: int = 8,
     token is written into the copy.  Otherwise the branch gets a fresh frame for it.
     """
     assert prompt_len % bs == 0
+    src = "f32" if kv_dtype == "f32" else "bf16"
     rng = np.random.default_rng(seed)
     nbr = prompts * branches
     tails = rng.integers(tail_lo, tail_hi + 1, size=nbr).astype(np.int64)
@@ -379,11 +380,11 @@ def fork_case(name: str, seed: int, *, prompts: int = 32, branches: int = 8,
         else:
             assert lb == len(row)
         tables[b, lb] = fresh[b]
-    q = _draw(rng, (nbr, Hq, D), std, "bf16")
-    pool_k = _draw(rng, (NB * bs, Hkv, D), std, "bf16")
-    pool_v = _draw(rng, (NB * bs, Hkv, D), std, "bf16")
-    new_k = _draw(rng, (nbr, Hkv, D), std, "bf16")
-    new_v = _draw(rng, (nbr, Hkv, D), std, "bf16")
+    q = _draw(rng, (nbr, Hq, D), std, src)
+    pool_k = _draw(rng, (NB * bs, Hkv, D), std, src)
+    pool_v = _draw(rng, (NB * bs, Hkv, D), std, src)
+    new_k = _draw(rng, (nbr, Hkv, D), std, src)
+    new_v = _draw(rng, (nbr, Hkv, D), std, src)
     live = np.zeros(NB * bs, dtype=bool)
     for p in range(prompts):
         f = prompt_frames[p].astype(np.int64)
@@ -394,12 +395,12 @@ def fork_case(name: str, seed: int, *, prompts: int = 32, branches: int = 8,
         live[f[pos // bs] * bs + pos % bs] = True
     new_slots = np.array([int(tables[b, (lens[b] - 1) // bs]) * bs + int((lens[b] - 1) % bs)
                           for b in range(nbr)], dtype=np.int64)
-    _poison(pool_k, pool_v, live, "bf16")
+    _poison(pool_k, pool_v, live, src)
     ks, vs = (1.0, 1.0)
     if kv_dtype == "fp8":
-        ks, vs = _fp8_scales(pool_k, pool_v, live, new_k, new_v, "bf16")
+        ks, vs = _fp8_scales(pool_k, pool_v, live, new_k, new_v, src)
     return DecodeCase(name=name, seed=seed, B=nbr, Hq=Hq, Hkv=Hkv, D=D, bs=bs, NB=NB,
-                      q_dtype="bf16", kv_dtype=kv_dtype, src_dtype="bf16",
+                      q_dtype=src, kv_dtype=kv_dtype, src_dtype=src,
                       scale=1.0 / math.sqrt(D), k_scale=ks, v_scale=vs,
                       context_lens=lens.astype(np.int32), block_tables=tables, q=q,
                       pool_k=pool_k, pool_v=pool_v, new_k=new_k, new_v=new_v,
