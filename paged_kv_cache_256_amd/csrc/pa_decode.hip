@@ -169,13 +169,13 @@ __global__ __launch_bounds__(kWaves * 64, GROUPED ? 1 : kWgPerCu) void decode_st
       NB, cap, qk_scale, v_scale, runs);
 }
 
-template <int KIND, int D, bool GROUPED>
+template <int KIND, int D, bool GROUPED, bool WIDE>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale, Runs runs,
     int B) {
-  decode_reduce_wave<KIND, D, GROUPED>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq, Hkv,
-                                       G, W, v_scale, runs, B);
+  decode_reduce_wave<KIND, D, GROUPED, WIDE>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq,
+                                             Hkv, G, W, v_scale, runs, B);
 }
 
 // Wavefronts of a launch: the full stream (3 per CU) unless the batch holds too few units for it.
@@ -239,7 +239,12 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
                      runs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  auto reduce_kernel = grouped ? decode_reduce_kernel<KIND, D, true> : decode_reduce_kernel<KIND, D, false>;
+  // few runs against the wavefronts (a few long sequences): each run is cut into many pieces,
+  // and the wide merge spreads them over more wavefronts and loads
+  const bool wide = !grouped && (long long)l.W >= 16LL * p.B * p.Hkv;
+  auto reduce_kernel = grouped ? decode_reduce_kernel<KIND, D, true, false>
+                       : wide  ? decode_reduce_kernel<KIND, D, false, true>
+                               : decode_reduce_kernel<KIND, D, false, false>;
   hipLaunchKernelGGL(reduce_kernel, dim3(l.W - 1), dim3(64), 0, stream, p.out, ws_ml, ws_o, plan,
                      p.Hq, p.Hkv, G, l.W, v_scale, runs, p.B);
   return hipGetLastError();

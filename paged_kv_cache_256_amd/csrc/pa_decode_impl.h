@@ -6,6 +6,8 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#include <type_traits>
+
 namespace pa {
 namespace dec {
 
@@ -550,24 +552,29 @@ __device__ __forceinline__ void decode_stream_wave(
 // the wavefronts holding the run's first and last frames; the run's partials are those of
 // wavefronts w0..w1 (any with an empty range hold none).  The merge is spread over those
 // boundary wavefronts by output columns: the first S of them (S a power of two, at most
-// w1 - w0 and at most D / 8) each merge a slice of D / S columns for every partial.  A run cut
+// w1 - w0 and at most D / 4) each merge a slice of D / S columns for every partial.  A run cut
 // once is merged by one wavefront; a run cut into ~100 pieces (one long sequence over the whole
-// GPU) by up to 16, each reading only its slice of the partials.  Wavefront w keeps a run in
+// GPU) by up to 32 (D = 128), each reading only its slice of the partials.  Wavefront w keeps a run in
 // partial slot 1 if the run began after the start of w's range (it is then w's last run), else
 // in slot 0.
 // Lanes: a slice's G x (D/S) outputs are held by groups of LPG lanes (row rr, QPL quads of
 // columns per lane); the 64 / LPG groups of the wavefront take the partials in turn (partial p by
-// group p mod groups), each with its own running (max, sum, accumulator), and the groups are
+// group p mod groups), each with its own running (max, sum, accumulator) and 16, 8 or 4 of its
+// partials loaded at once (one, two or more quads per lane), and the groups are
 // combined by the same rule with lane swaps at the end.  The merge order depends only on the
 // sizes, so equal inputs give equal bits.  (GROUPED: a run's rows are its members' heads, row r
 // being head r % G of member r / G.)
-template <int KIND, int D, bool GROUPED = false>
+// WIDE (launches whose runs are few against the wavefronts, i.e. a few long sequences): slices
+// down to one quad per row (S at most D / 4), and groups with more than 4 partials load 8 or 16
+// of them at once.  Other launches keep S at most D / 8 and batches of 4, a smaller kernel.
+template <int KIND, int D, bool GROUPED = false, bool WIDE = false>
 __device__ __forceinline__ void decode_reduce_wave(
     int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale,
     Runs runs = Runs{}, int B = 0) {
-  // partials per group in flight together (8 take ~330 registers and made the merge of the
-  // 70B-shape batch 6.8 us instead of 4.6 us)
+  // partials per group in flight together when a lane holds more than two quads of a row (8
+  // took ~330 registers and made the merge of the 70B-shape batch 6.8 us instead of 4.6 us);
+  // lanes with one or two quads keep 16 or 8 in flight
   constexpr int kBatch = 4;
   constexpr int NV = D / 16;  // quads per lane at most (G = 16, one slice)
   const int U = plan[0];
@@ -583,7 +590,7 @@ __device__ __forceinline__ void decode_reduce_wave(
   const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
   const int cuts = w1 - w0;  // boundaries cutting the run's frames, k among them
   int S = 1;
-  while (2 * S <= cuts && 2 * S <= D / 8) S *= 2;
+  while (2 * S <= cuts && 2 * S <= (WIDE ? D / 4 : D / 8)) S *= 2;
   const int sl = k - w0;  // this wavefront's slice
   if (sl >= S) return;
   const int b = st.x, g = st.y;
@@ -606,37 +613,87 @@ __device__ __forceinline__ void decode_reduce_wave(
   for (int v = 0; v < NV; ++v) num[v] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const long long aw0 = F * w0 / W;
   const bool dense = F >= W;  // no empty ranges: every wavefront w0..w1 holds a partial
-  for (int wb = w0 + grp; wb <= w1; wb += kBatch * groups) {
-    f32x4 ob[kBatch][NV];
-    float mb[kBatch], lb[kBatch];
+  // the group's partials, QPL quads each, BATCH of them loaded before any is used
+  auto merge = [&](auto qpl_c, auto batch_c) {
+    constexpr int QPL = decltype(qpl_c)::value, BATCH = decltype(batch_c)::value;
+    for (int wb = w0 + grp; wb <= w1; wb += BATCH * groups) {
+      f32x4 ob[BATCH][QPL];
+      float mb[BATCH], lb[BATCH];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int w = wb + i * groups;
-      bool has = w <= w1;
-      if (!dense && has) has = F * w / W < F * (w + 1) / W;
-      if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
-      const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
-      const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
-      const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
+      for (int i = 0; i < BATCH; ++i) {
+        const int w = wb + i * groups;
+        bool has = w <= w1;
+        if (!dense && has) has = F * w / W < F * (w + 1) / W;
+        if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
+        const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
+        const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
+        const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) ob[i][v] = (has && v < qpl) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
-      mb[i] = has ? ws_ml[2 * prow] : -INFINITY;
-      lb[i] = has ? ws_ml[2 * prow + 1] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      if (mb[i] == -INFINITY) continue;
-      if (mb[i] > M) {
-        const float sc = __builtin_amdgcn_exp2f(M - mb[i]);
-        den *= sc;
-#pragma unroll
-        for (int v = 0; v < NV; ++v) num[v] *= sc;
-        M = mb[i];
+        for (int v = 0; v < QPL; ++v) ob[i][v] = (has && v < qpl) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        mb[i] = has ? ws_ml[2 * prow] : -INFINITY;
+        lb[i] = has ? ws_ml[2 * prow + 1] : 0.f;
       }
-      const float ew = __builtin_amdgcn_exp2f(mb[i] - M);
-      den += ew * lb[i];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) num[v] += ew * ob[i][v];
+      for (int i = 0; i < BATCH; ++i) {
+        if (mb[i] == -INFINITY) continue;
+        if (mb[i] > M) {
+          const float sc = __builtin_amdgcn_exp2f(M - mb[i]);
+          den *= sc;
+#pragma unroll
+          for (int v = 0; v < QPL; ++v) num[v] *= sc;
+          M = mb[i];
+        }
+        const float ew = __builtin_amdgcn_exp2f(mb[i] - M);
+        den += ew * lb[i];
+#pragma unroll
+        for (int v = 0; v < QPL; ++v) num[v] += ew * ob[i][v];
+      }
+    }
+  };
+  // (the batch size sets only how many loads are in flight: partials are merged in the same
+  // order, so every choice gives the same bits)
+  if constexpr (WIDE) {
+    const int per_group = (w1 - w0 + groups) / groups;  // partials of a group, at most
+    if (qpl == 1 && per_group > 8) {
+      merge(std::integral_constant<int, 1>{}, std::integral_constant<int, 16>{});
+    } else if (qpl <= 2 && per_group > kBatch) {
+      merge(std::integral_constant<int, 2>{}, std::integral_constant<int, 8>{});
+    } else {
+      merge(std::integral_constant<int, NV>{}, std::integral_constant<int, kBatch>{});
+    }
+  } else {
+    for (int wb = w0 + grp; wb <= w1; wb += kBatch * groups) {
+      f32x4 ob[kBatch][NV];
+      float mb[kBatch], lb[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int w = wb + i * groups;
+        bool has = w <= w1;
+        if (!dense && has) has = F * w / W < F * (w + 1) / W;
+        if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
+        const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
+        const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
+        const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) ob[i][v] = (has && v < qpl) ? src[v] : (f32x4){0.f, 0.f, 0.f, 0.f};
+        mb[i] = has ? ws_ml[2 * prow] : -INFINITY;
+        lb[i] = has ? ws_ml[2 * prow + 1] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        if (mb[i] == -INFINITY) continue;
+        if (mb[i] > M) {
+          const float sc = __builtin_amdgcn_exp2f(M - mb[i]);
+          den *= sc;
+#pragma unroll
+          for (int v = 0; v < NV; ++v) num[v] *= sc;
+          M = mb[i];
+        }
+        const float ew = __builtin_amdgcn_exp2f(mb[i] - M);
+        den += ew * lb[i];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) num[v] += ew * ob[i][v];
+      }
     }
   }
   // combine the groups: after the swap at distance d, each lane holds the merge of its group
