@@ -198,13 +198,16 @@ class DeviceState:
                               k_scale=c.k_scale, v_scale=c.v_scale, out=self.cout,
                               workspace=self.cws, prepared=prepared)
 
-    def init_shared(self, dev):
+    def init_shared(self, dev, max_run=None):
         """Runs of consecutive sequences that share their tables' first frames (found on the host,
-        like the block tables a scheduler hands over) for pa_decode_shared."""
+        like the block tables a scheduler hands over) for pa_decode_shared: at most max_run
+        sequences a run (default: as many as the run's score columns hold)."""
         c, pa = self.c, self.pa
         import torch
 
-        r = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs, max(1, 16 // (c.Hq // c.Hkv)))
+        most = max(1, pa.SHARED_RUN_COLUMNS // (c.Hq // c.Hkv))
+        r = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs,
+                                    min(most, max_run) if max_run else most)
         self.groups = r.to(dev)
         need = pa.decode_shared_workspace_bytes(c.B, c.Hq, c.D, c.bs, c.kv_dtype, c.max_context_len)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -253,6 +256,9 @@ def main():
     ap.add_argument("--shared-prefix", action="store_true",
                     help="decode with pa_decode_shared: sequences whose tables begin with the same "
                          "frames (config 4's branches) read them once per group")
+    ap.add_argument("--shared-run-max", type=int, default=None,
+                    help="with --shared-prefix: at most this many sequences a run (default: as "
+                         "many as a run's score columns hold)")
     ap.add_argument("--long", type=int, default=None, choices=[1, 4, 16],
                     help="long-context decode instead of a named config: this many sequences of "
                          "32,768 tokens at the 70B layer shape")
@@ -294,7 +300,7 @@ def main():
         if not case.B:
             print("bench.py: --shared-prefix needs decodes", file=sys.stderr)
             sys.exit(2)
-        groups = st.init_shared(dev)
+        groups = st.init_shared(dev, args.shared_run_max)
         log(f"[bench] {groups.num_runs} runs of sequences that share their first frames")
     torch.cuda.synchronize()
     log(f"[bench] caches filled on the GPU ({case.NB} frames)")
@@ -405,6 +411,9 @@ def main():
                                 "pa_prefill_chunk + pa_decode" if case.chunk is not None and case.B else
                                 "pa_prefill_chunk" if case.chunk is not None else "pa_decode",
              "decode_shared_frames_hint": bool(case.B and st.shared)}
+    if groups is not None:
+        extra["shared_runs"] = groups.num_runs
+        extra["shared_run_max"] = int(np.max(groups.run_size)) if len(groups.run_size) else 0
     if case.B and case.shares_frames:
         # frames several sequences reference are one copy in HBM: the bytes a decode that reads
         # each referenced frame once must move

@@ -80,6 +80,10 @@ enum {
   PA_ENOSPC = -5   /* the workspace is smaller than the *_workspace_bytes result */
 };
 
+/* Score columns of one run of pa_decode_shared: a run of s sequences needs s * G of them
+ * (G = Hq / Hkv query heads per KV head). */
+#define PA_SHARED_RUN_COLUMNS 16
+
 /* Message describing the last failure on the calling thread ("" after success). */
 const char* pa_last_error(void);
 
@@ -196,16 +200,16 @@ int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void*
  * search, which reference the prompt's frames instead of copying them (bicarait.com,
  * "Architectural Blueprint 2" and "Physical Memory Sharing"; infoisland, section 2).  The result
  * is pa_decode's (to fp32 rounding); the shared frames are read once per run instead of once per
- * sequence.  A run's members put their G query heads side by side in the 16 columns of the
- * matrix-core score tile (at G = 8 a plain decode leaves half of them empty): the run streams
- * the shared frames once for all members, then each member's own frames with the other members'
- * columns masked, with one online softmax per column.
+ * sequence.  A run's members put their G query heads side by side in the PA_SHARED_RUN_COLUMNS
+ * (16) columns of the matrix-core score tile (at G = 8 a plain decode leaves half of them
+ * empty): the run streams the shared frames once for all members, then each member's own frames
+ * with the other members' columns masked, with one online softmax per column.
  *   Arguments shared with pa_decode have its meaning, except the workspace: at least
  *   pa_decode_shared_workspace_bytes(...) bytes (the launch runs more wavefronts than
  *   pa_decode's), 256-byte aligned.
  *   run_size       int32 [B], device: run_size[b] = s >= 1 starts a run of the sequences
  *                  [b, b + s); 0 marks a sequence inside a run.  Every sequence is in one run;
- *                  s * G <= 16 (G = Hq / Hkv).
+ *                  s * G <= PA_SHARED_RUN_COLUMNS (G = Hq / Hkv).
  *   shared_blocks  int32 [B], device: the block-table entries the members of b's run share (the
  *                  same for all members; 0 for a run of one).  The members' first
  *                  shared_blocks[b] entries are equal, and shared_blocks[b] * block_size <
@@ -226,7 +230,8 @@ int pa_decode_shared(void* out, const void* q, const void* k_cache, const void* 
 /*
  * pa_find_shared_prefixes -- host-only: runs for pa_decode_shared, found in host copies of a
  * batch's block tables and context lengths.  From each sequence on, the longest stretch of at most
- * max_run (1 .. 16; 16 / G for pa_decode_shared) consecutive sequences whose tables agree on at
+ * max_run (1 .. PA_SHARED_RUN_COLUMNS; PA_SHARED_RUN_COLUMNS / G for pa_decode_shared)
+ * consecutive sequences whose tables agree on at
  * least their first entry becomes a run; its shared blocks are the leading entries all members
  * agree on, limited to the blocks before each member's last token.  Sequences that join no such
  * stretch are runs of one.  Outputs: shared_blocks and run_size (int32 [B] each), and
@@ -368,7 +373,8 @@ int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_se
                               int num_decodes, int num_chunks, int block_size, int64_t NB,
                               int max_chunk_len, int max_context_len);
 /*  pa_validate_shared_prefixes: run_size and shared_blocks cut the batch into runs as
- *    pa_decode_shared requires (every sequence in one run of at most 16 / G sequences, equal
+ *    pa_decode_shared requires (every sequence in one run of at most PA_SHARED_RUN_COLUMNS / G
+ *    sequences, equal
  *    shared blocks within a run, 0 for runs of one, equal shared table entries, context lengths
  *    above the shared blocks' tokens). */
 int pa_validate_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,

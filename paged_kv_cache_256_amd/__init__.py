@@ -28,6 +28,7 @@ from ._binding import (  # noqa: F401
     decode_workspace_bytes,
     find_shared_prefixes,
     SharedRuns,
+    SHARED_RUN_COLUMNS,
     last_error,
     lib,
     mixed_attention,

@@ -289,6 +289,11 @@ def decode_noalloc(q, k_cache, v_cache, block_tables, context_lens, *, block_siz
     return out
 
 
+# Score columns of one run of pa_decode_shared (PA_SHARED_RUN_COLUMNS): a run of s sequences
+# needs s * G of them.
+SHARED_RUN_COLUMNS = 16
+
+
 class SharedRuns:
     """Runs of consecutive sequences that share the first frames of their block tables
     (pa_decode_shared): run_size[b] >= 1 starts a run of run_size[b] sequences, 0 marks a

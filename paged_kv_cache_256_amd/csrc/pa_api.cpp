@@ -16,6 +16,8 @@
 #include "pa.h"
 #include "pa_internal.h"
 
+static_assert(pa::kSharedRunColumns == PA_SHARED_RUN_COLUMNS, "run columns of the kernels");
+
 namespace {
 thread_local std::string g_error;
 }  // namespace
@@ -538,7 +540,8 @@ int pa_validate_mixed_indices(const int32_t* block_tables, int max_blocks_per_se
 int pa_find_shared_prefixes(const int32_t* block_tables, int max_blocks_per_seq,
                             const int32_t* context_lens, int B, int block_size, int max_run,
                             int32_t* shared_blocks, int32_t* run_size, int* num_runs) {
-  if (B < 0 || max_blocks_per_seq < 1 || block_size < 1 || max_run < 1 || max_run > 16)
+  if (B < 0 || max_blocks_per_seq < 1 || block_size < 1 || max_run < 1 ||
+      max_run > PA_SHARED_RUN_COLUMNS)
     return fail(PA_EINVAL, "bad sizes (B %d, max_blocks_per_seq %d, block_size %d, max_run %d)",
                 B, max_blocks_per_seq, block_size, max_run);
   if (!num_runs || (B > 0 && (!block_tables || !context_lens || !shared_blocks || !run_size)))
@@ -590,8 +593,9 @@ int pa_validate_shared_prefixes(const int32_t* block_tables, int max_blocks_per_
     const int s = run_size[b];
     if (s < 1) return fail(PA_EINVAL, "run_size[%d] = %d: sequence %d starts no run and is in none", b, s, b);
     if (b + s > B) return fail(PA_ERANGE, "run at %d of %d sequences runs past the batch", b, s);
-    if (s * G > 16)
-      return fail(PA_ERANGE, "run at %d has %d sequences: %d x %d query heads exceed 16 columns", b, s, s, G);
+    if ((long long)s * G > PA_SHARED_RUN_COLUMNS)
+      return fail(PA_ERANGE, "run at %d has %d sequences: %d x %d query heads exceed %d columns", b,
+                  s, s, G, PA_SHARED_RUN_COLUMNS);
     const int P = shared_blocks[b];
     if (s == 1 && P != 0) return fail(PA_EINVAL, "shared_blocks[%d] = %d for a run of one", b, P);
     if (P < 0 || P > max_blocks_per_seq) return fail(PA_ERANGE, "shared_blocks[%d] = %d", b, P);

@@ -93,6 +93,8 @@ int clear_error();
 int device_compute_units();
 
 size_t decode_workspace_bytes(int B, int Hq, int D, int bs, int kv_dtype, int max_context_len);
+// Score columns of one run of sequences that share frames (one matrix-core tile).
+constexpr int kSharedRunColumns = 16;
 // Workspace of a decode over runs of sequences that share frames (more wavefronts per CU).
 size_t decode_shared_workspace_bytes(int D);
 // The allocation-free decode's device scratch: kDecodeScratchBytes per GPU, in a file-scope

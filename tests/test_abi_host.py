@@ -471,6 +471,22 @@ def test_find_shared_prefixes_makes_runs_of_consecutive_sequences():
         pa.validate_shared_prefixes(tables, lens, bs, r, 8)  # a run of 3 at G = 8
 
 
+def test_run_column_limit_matches_the_header_and_bounds_the_finder():
+    hdr = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"#define PA_SHARED_RUN_COLUMNS (\d+)", hdr)
+    assert m and int(m.group(1)) == pa.SHARED_RUN_COLUMNS == 16
+    tables = np.arange(40, dtype=np.int32).reshape(40, 1) * 0 + 7  # 40 sequences, one frame 7
+    lens = np.full(40, 20, np.int32)  # 16-token blocks: frame 7 full, the last token in frame 2
+    tables = np.concatenate([tables, np.arange(40, dtype=np.int32).reshape(40, 1) + 100], axis=1)
+    r = pa.find_shared_prefixes(tables, lens, 16, pa.SHARED_RUN_COLUMNS)
+    assert r.run_size.tolist()[:2] == [16, 0] and r.run_size[16] == 16 and r.run_size[32] == 8
+    pa.validate_shared_prefixes(tables, lens, 16, r, 1)
+    with pytest.raises(pa.PAError, match="exceed 16 columns"):
+        pa.validate_shared_prefixes(tables, lens, 16, r, 2)  # a run of 16 at G = 2
+    with pytest.raises(pa.PAError):
+        pa.find_shared_prefixes(tables, lens, 16, pa.SHARED_RUN_COLUMNS + 1)
+
+
 def test_validate_shared_prefixes_rejects_inconsistent_runs():
     bs = 16
     tables = np.array([[5, 6, 7], [5, 6, 8], [5, 9, 1]], np.int32)

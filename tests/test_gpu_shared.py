@@ -51,7 +51,8 @@ def _check(c, g, runs):
 
 def test_config4_every_output():
     c = workloads.make(4)
-    runs = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs, 16 // (c.Hq // c.Hkv))
+    runs = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs,
+                                   pa.SHARED_RUN_COLUMNS // (c.Hq // c.Hkv))
     assert runs.num_runs == 128 and set(runs.run_size.tolist()) == {0, 2}
     g = GpuStep(c)
     g.write()
