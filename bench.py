@@ -402,6 +402,7 @@ def main():
                 "traffic_source": traffic[1] if traffic else None}
     extra = {"write_us": round(float(write_ms.mean()) * 1e3, 2),
              "decode_us": round(dec_avg * 1e3, 2),
+             "decode_us_median": round(float(np.median(dec_ms)) * 1e3, 2),
              "decode_us_p10_p90": [round(float(np.percentile(dec_ms, 10)) * 1e3, 2),
                                    round(float(np.percentile(dec_ms, 90)) * 1e3, 2)],
              "wall_s_timed_loop": round(wall, 3), "flush_between_steps": flush is not None,
