@@ -20,12 +20,15 @@ struct PQ {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// One LDS-DMA copy (global_load_lds_dwordx4): each lane's 16 bytes at src land at lds + 16 lane.
-// Issued as assembly so that the compiler does not make unrelated LDS reads wait for it (the
-// pipeline below waits for the copies itself); the kernels that use it leave M0 to it.
-__device__ inline void lds_dma16(const void* src, uint32_t lds_addr) {
+// One LDS-DMA copy (global_load_lds_dwordx4): each lane's 16 bytes at sbase + voff land at
+// lds + 16 lane.  sbase is wavefront-uniform (the instruction's scalar base) and voff a lane's
+// 32-bit offset, so the per-copy address work is scalar.  Issued as assembly so that the
+// compiler does not make unrelated LDS reads wait for it (the pipeline below waits for the
+// copies itself); the kernels that use it leave M0 to it.
+__device__ inline void lds_dma16(const char* sbase, uint32_t voff, uint32_t lds_addr) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(sbase), "s"(base)
                : "memory");
 }
 
@@ -150,11 +153,15 @@ __device__ __forceinline__ void prefill_tile(
     }
   }
 
-  float m[NT], lsum[NT];
+  // m: each row's running shift; mth = m + kLazy (the bound a stage's scores are tested
+  // against) and nm = -m (0 while m = -inf: the exponentials' offset) change only with m
+  float m[NT], mth[NT], nm[NT], lsum[NT];
   f32x4 acc[NT][NC];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     m[t] = -INFINITY;
+    mth[t] = -INFINITY;
+    nm[t] = 0.f;
     lsum[t] = 0.f;
 #pragma unroll
     for (int cc = 0; cc < NC; ++cc) acc[t][cc] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -217,11 +224,10 @@ __device__ __forceinline__ void prefill_tile(
 #pragma unroll
       for (int z = 1; z < SF; ++z)
         if (fl == z) t = tix[z];
-      // frames past the range and invalid ids copy 16 bytes of tile 0 into every lane's slot
-      // (never used): every stage issues the same copies, so the wait counts below hold
+      // frames past the range and invalid ids copy block r of tile 0 instead (never used):
+      // every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      const char* src = base + (size_t)(uint32_t)max(t, 0) * TILE_S + r * 1024 + (t >= 0 ? lane16 : 0);
-      lds_dma16(src, buf_lds + blk * 1024);
+      lds_dma16(base + (size_t)(uint32_t)max(t, 0) * TILE_S + r * 1024, lane16, buf_lds + blk * 1024);
     }
     if (next) {
       // the window after the new one, requested after this stage's copies
@@ -287,7 +293,11 @@ __device__ __forceinline__ void prefill_tile(
             s[t][gi][ii] = (key < kend && key <= rpos[t]) ? s[t][gi][ii] : -INFINITY;
           }
     }
-    float mxs[NT];
+    // A row's stage maximum exceeds m + kLazy exactly when the maximum over one of its lanes'
+    // keys does (scaling by qk_abs > 0 keeps the order), so the decision is taken on each lane's
+    // own maximum, and the maxima are reduced across the row's lanes only on the stages where the
+    // shift moves.
+    float lmx[NT];
     bool grow = false;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -296,17 +306,19 @@ __device__ __forceinline__ void prefill_tile(
       for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii) mx = fmaxf(mx, s[t][gi][ii]);
-      mx = wave_max_over_j(mx);
-      mx = mx == -INFINITY ? -INFINITY : mx * qk_abs;  // scores scale by qk_abs >= 0
-      mxs[t] = mx;
-      grow = grow || mx > m[t] + kLazy;
+      lmx[t] = mx;
+      grow = grow || mx * qk_abs > mth[t];  // (-inf * qk_abs is -inf: never grows)
     }
     if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const float mnew = fmaxf(m[t], mxs[t]);
+        float mx = wave_max_over_j(lmx[t]);
+        mx = mx == -INFINITY ? -INFINITY : mx * qk_abs;  // scores scale by qk_abs >= 0
+        const float mnew = fmaxf(m[t], mx);
         const float alpha = m[t] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[t] - mnew);
         m[t] = mnew;
+        mth[t] = mnew + kLazy;
+        nm[t] = mnew == -INFINITY ? 0.f : -mnew;
         lsum[t] *= alpha;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc) acc[t][cc] *= alpha;
@@ -318,9 +330,6 @@ __device__ __forceinline__ void prefill_tile(
     // the next pair's work); splitting the stage into pairs keeps the registers in flight to
     // about one pair's worth (the whole stage as one block spills).
     const bool tail = key0 + SK > kend;
-    float nm[NT];  // the exponentials' shift
-#pragma unroll
-    for (int t = 0; t < NT; ++t) nm[t] = m[t] == -INFINITY ? 0.f : -m[t];
     // P * V over pairs of 16-key groups (one 16x16x32 product each); with 16-key frames the two
     // groups are two frames, with 32-key frames the two halves of one
 #pragma unroll
