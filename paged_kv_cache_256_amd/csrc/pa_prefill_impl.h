@@ -20,16 +20,32 @@ struct PQ {
   static constexpr int bytes = KIND == KF32 ? 4 : 2;
 };
 
-// One LDS-DMA copy (global_load_lds_dwordx4): each lane's 16 bytes at sbase + voff land at
-// lds + 16 lane.  sbase is wavefront-uniform (the instruction's scalar base) and voff a lane's
-// 32-bit offset, so the per-copy address work is scalar.  Issued as assembly so that the
-// compiler does not make unrelated LDS reads wait for it (the pipeline below waits for the
-// copies itself); the kernels that use it leave M0 to it.
-__device__ inline void lds_dma16(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+// N consecutive LDS-DMA copies (global_load_lds_dwordx4) of 1 KiB blocks: block i is read at
+// sbase + 1024 i and lands at lds + 1024 i, each lane's 16 bytes at the lane's offset voff in the
+// block (voff = 16 lane).  sbase is wavefront-uniform (the instruction's scalar base); the
+// instruction's immediate offset moves the global and the LDS address together, so one M0 and
+// one base serve the N blocks.  Issued as assembly so that the compiler does not make unrelated
+// LDS reads wait for the copies (the pipeline below waits for them itself); the kernels that use
+// it leave M0 to it.
+template <int N>
+__device__ inline void lds_dma16_run(const char* sbase, uint32_t voff, uint32_t lds_addr) {
+  static_assert(N == 1 || N == 2 || N == 4, "1, 2 or 4 blocks");
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
-               "s"(sbase), "s"(base)
-               : "memory");
+  if constexpr (N == 1) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+                 "s"(sbase), "s"(base)
+                 : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024" ::"v"(voff), "s"(sbase), "s"(base)
+                 : "memory");
+  } else {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:3072" ::"v"(voff), "s"(sbase), "s"(base)
+                 : "memory");
+  }
 }
 
 // The 32-bit LDS address of a pointer into a __shared__ buffer.
@@ -131,7 +147,10 @@ __device__ __forceinline__ void prefill_tile(
   const uint32_t qsign = qk_scale < 0.f ? (KIND == KF32 ? 0x80000000u : 0x80008000u) : 0u;
   uint32_t qw[NT][QW];
   int rpos[NT];
-  int rmin[NT];  // position of the tile's first row (the smallest), or -1 past the chunk
+  // The largest key every row of this wavefront's tiles may see: keys past it (past a tile's
+  // first row, whose position is the tile's smallest, or at or past kend) need the mask.  A tile
+  // past the chunk counts as position -1.
+  int lim = kend - 1;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int qrow = (w * NT + t) * 16 + n;
@@ -140,7 +159,7 @@ __device__ __forceinline__ void prefill_tile(
     rpos[t] = ok ? pos0 + tok : -1;
     {
       const int tok0 = t0 + (w * NT + t) * 16 / G;
-      rmin[t] = tok0 < C ? pos0 + tok0 : -1;
+      lim = min(lim, tok0 < C ? pos0 + tok0 : -1);
     }
     const size_t row = (size_t)(r0 + (ok ? tok : 0)) * Hq + (size_t)g * G + qrow % G;
     const u32x4* src = (const u32x4*)((const char*)q + (row * D + (size_t)(D / 4) * j) * QB);
@@ -168,17 +187,20 @@ __device__ __forceinline__ void prefill_tile(
   }
 
   const int nst = (kend - kbeg + SK - 1) / SK;
+  // the stage whose keys reach past kend (the last, unless the range is whole stages), or -1
+  const int tail_st = (kend - kbeg) % SK ? nst - 1 : -1;
   const size_t trow = (size_t)c * mbps;
 
   // Staging of a stage: its K and V tiles are NBLK blocks of 1 KiB in the cache's tile
   // layout (a block holds one 16-byte fragment per lane), stored in LDS as [frame][K, V][block].
-  // Wavefront w copies blocks w, w + 8, ... straight from global memory into the stage's LDS
-  // buffer with LDS-DMA loads (lane l's 16 bytes land at the block's base + 16 l): no register or
-  // LDS store of the wavefront carries them, and the copy of a later stage runs while this one
-  // is computed.
+  // Wavefront w copies the BPW consecutive blocks w BPW, ..., all of one K or V tile, straight
+  // from global memory into the stage's LDS buffer with LDS-DMA loads (lane l's 16 bytes land at
+  // the block's base + 16 l): no register or LDS store of the wavefront carries them, and the
+  // copy of a later stage runs while this one is computed.
   constexpr int NBLK = STAGE / 1024;
   constexpr int BPW = (NBLK + kPWaves - 1) / kPWaves;  // blocks per wavefront and stage
   static_assert(NBLK % kPWaves == 0 || NBLK < kPWaves, "stage blocks must split over waves");
+  static_assert(NLS % BPW == 0, "a wavefront's blocks lie in one tile");
   static_assert(64 % SF == 0, "a stage's frames lie in one window of 64 block ids");
   // Block ids come in windows of 64 frames, one per lane, fetched one window ahead with a single
   // vector load: lane l of window wi loads the table entry of frame kbeg / BS + 64 wi + l (the
@@ -211,23 +233,15 @@ __device__ __forceinline__ void prefill_tile(
       tix_cur = tiles_of(raw_nxt, wi);
       win = wi;
     }
-    int tix[SF];
-#pragma unroll
-    for (int fl = 0; fl < SF; ++fl) tix[fl] = __builtin_amdgcn_readlane(tix_cur, (st * SF + fl) & 63);
-    const uint32_t buf_lds = lds_address(buf);
-#pragma unroll
-    for (int k = 0; k < BPW; ++k) {
-      const int blk = w + k * kPWaves;
-      if (NBLK < kPWaves && blk >= NBLK) break;  // wavefront-uniform
+    const int blk = w * BPW;  // (wavefront-uniform)
+    if (NBLK >= kPWaves || blk < NBLK) {
       const int fl = blk / (2 * NLS), kind = (blk / NLS) & 1, r = blk % NLS;
-      int t = tix[0];
-#pragma unroll
-      for (int z = 1; z < SF; ++z)
-        if (fl == z) t = tix[z];
-      // frames past the range and invalid ids copy block r of tile 0 instead (never used):
+      const int t = __builtin_amdgcn_readlane(tix_cur, (st * SF + fl) & 63);
+      // frames past the range and invalid ids copy blocks of tile 0 instead (never used):
       // every stage issues the same copies, so the wait counts below hold
       const char* base = kind ? v_cache : k_cache;
-      lds_dma16(base + (size_t)(uint32_t)max(t, 0) * TILE_S + r * 1024, lane16, buf_lds + blk * 1024);
+      lds_dma16_run<BPW>(base + (size_t)(uint32_t)max(t, 0) * TILE_S + r * 1024, lane16,
+                         lds_address(buf) + blk * 1024);
     }
     if (next) {
       // the window after the new one, requested after this stage's copies
@@ -279,10 +293,7 @@ __device__ __forceinline__ void prefill_tile(
     // One wavefront-uniform rescale decision per stage keeps the accumulators in place.  The
     // causal / range mask is applied only on stages that reach past a row's position or the
     // range end.
-    bool masked = key0 + SK > kend;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) masked = masked || key0 + SK - 1 > rmin[t];
-    if (masked) {
+    if (key0 + SK - 1 > lim) {  // (wavefront-uniform; true from some stage on)
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -329,7 +340,7 @@ __device__ __forceinline__ void prefill_tile(
     // interleaves the score products with the exponentials (and the P.V products of a pair with
     // the next pair's work); splitting the stage into pairs keeps the registers in flight to
     // about one pair's worth (the whole stage as one block spills).
-    const bool tail = key0 + SK > kend;
+    const bool tail = st == tail_st;  // (key0 + SK > kend)
     // P * V over pairs of 16-key groups (one 16x16x32 product each); with 16-key frames the two
     // groups are two frames, with 32-key frames the two halves of one
 #pragma unroll
