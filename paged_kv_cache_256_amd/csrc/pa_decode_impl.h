@@ -32,6 +32,9 @@ inline int stream_waves() {
 // after the run starts, about four frames of a wavefront's streaming time at 3 wavefronts per CU;
 // 3 to 6 measure alike and 1.5% faster than 2 over four 70B-shape batches).
 constexpr int kRestart = 4;
+
+// log2-domain slack before a run's running shift moves (its accumulators are then rescaled)
+constexpr float kLazyShift = 8.f;
 __host__ __device__ inline int run_units(int nblk) { return nblk > 0 ? nblk + kRestart : 0; }
 
 // Tile loads: non-temporal (not retained in the caches) when every frame is read once per call;
@@ -194,7 +197,14 @@ __device__ __forceinline__ void decode_stream_wave(
   const long long a = range_begin(Ftot, w, W), e = range_begin(Ftot, w + 1, W);
   if (a >= e) return;
 
-  float m = -INFINITY, lsum = 0.f;
+  // Scores scale by qk_abs >= 0; a negative scale goes into the query's sign bits (exact).  (A zero
+  // scale is replaced by 1e-30: every product is then far below half an ulp of the shift, so each
+  // probability is exactly 1, and -inf * qk_abs stays -inf.)
+  const float qk_abs = fmaxf(fabsf(qk_scale), 1e-30f);
+  const uint32_t qsign = qk_scale < 0.f ? (KIND == KF32 ? 0x80000000u : 0x80008000u) : 0u;
+  // m: the running shift of the scaled scores (lazily moved); mth = m + kLazyShift, and nm = -m
+  // (0 while m = -inf), the exponentials' offset, change only with m
+  float m = -INFINITY, mth = -INFINITY, nm = 0.f, lsum = 0.f;
   f32x4 acc[NC];
   uint32_t qw[QW];
 
@@ -216,22 +226,32 @@ __device__ __forceinline__ void decode_stream_wave(
     for (int f = 0; f < F; ++f) {
       const int i = min(s * F + f, 63);
       const int fr = __builtin_amdgcn_readlane(fid, i);
-      const int ls = lane * __builtin_amdgcn_readlane(fstride, i);
-      const u32x4* kp = (const u32x4*)(k_cache + ((size_t)fr * Hkv + gg) * TILE) + ls;
-      const u32x4* vp = (const u32x4*)(v_cache + ((size_t)fr * Hkv + gg) * TILE) + ls;
+      // the tile's address is wavefront-uniform and a lane's offset is 16 lane or 0: the loads
+      // take the tile address as their scalar base
+      const uint32_t off = __builtin_amdgcn_readlane(fstride, i) ? 16u * (uint32_t)lane : 0u;
+      const char* kb = k_cache + ((size_t)fr * Hkv + gg) * TILE + off;
+      const char* vb = v_cache + ((size_t)fr * Hkv + gg) * TILE + off;
 #pragma unroll
-      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16<NT>(kp + r * 64);
+      for (int r = 0; r < NL; ++r) kt[f][r] = load_tile16<NT>((const u32x4*)(kb + r * 1024));
 #pragma unroll
-      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16<NT>(vp + r * 64);
+      for (int r = 0; r < NL; ++r) vt[f][r] = load_tile16<NT>((const u32x4*)(vb + r * 1024));
     }
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // Consume step s of the current chunk.  No loads in here: the only branch between a step's
   // loads and this use is the loop back-edge, so the next step's loads stay in flight.
+  // Online softmax with a lazily moved shift: the accumulators are rescaled only when a step's
+  // scaled scores exceed m + kLazyShift (log2 domain); otherwise the step's probabilities
+  // exp2(s - m) may exceed 1 by at most 2^kLazyShift, which changes neither the normalised result
+  // nor the fp32 accumulation.  A row's step maximum exceeds the bound exactly when one of its
+  // lanes' does (scaling by qk_abs > 0 keeps the order), so each lane tests its own maximum and
+  // the row maxima are reduced across lanes only on the steps where the shift moves.  Keys are
+  // masked only in frames that need it (the context's last frame, dead frames, and member
+  // columns of a grouped run).
   auto compute_step = [&](u32x4 (&kt)[F][NL], u32x4 (&vt)[F][NL], int s) {
     f32x4 sc[NGS];
-    float mx = -INFINITY;
+    float lmx = -INFINITY;
 #pragma unroll
     for (int f = 0; f < F; ++f) {
       const int i = s * F + f;
@@ -242,14 +262,18 @@ __device__ __forceinline__ void decode_stream_wave(
         f32x4 sv = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int sl = 0; sl < NS; ++sl) sv = Ops::qk(sv, Ops::kop(kt[f], h, sl), Ops::qop(qw, sl));
+        sc[f * KG + h] = sv;
+      }
+      const bool cols = GROUPED && (col0 > 0 || col1 < 16);  // (wavefront-uniform)
+      if (valid < BS || cols) {
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-          bool keep = 16 * h + 4 * j + ii < valid;
-          if constexpr (GROUPED) keep = keep && n >= col0 && n < col1;
-          const float v = keep ? sv[ii] * qk_scale : -INFINITY;
-          sc[f * KG + h][ii] = v;
-          mx = fmaxf(mx, v);
-        }
+        for (int h = 0; h < KG; ++h)
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            bool keep = 16 * h + 4 * j + ii < valid;
+            if constexpr (GROUPED) keep = keep && n >= col0 && n < col1;
+            sc[f * KG + h][ii] = keep ? sc[f * KG + h][ii] : -INFINITY;
+          }
       }
       if (valid < BS) {
         // dead frame, or the last frame of the context: clear V of the slots outside it so that
@@ -261,30 +285,31 @@ __device__ __forceinline__ void decode_stream_wave(
           for (int c = 0; c < NC; ++c) Ops::zero_quad(vt[f], h, c, keep);
         }
       }
-    }
-    mx = wave_max_over_j(mx);
-    const float mnew = fmaxf(m, mx);
-    float mref = mnew;  // the exponentials' shift
-    if constexpr (GROUPED) {
-      // a member's columns may have seen no key yet while another member's are live: the step is
-      // skipped only when no column has, and a column still at -inf shifts by 0 (its
-      // probabilities are exp2(-inf) = 0 and its state stays empty)
-      if (!__builtin_amdgcn_ballot_w64(mnew != -INFINITY)) return;
-      mref = mnew == -INFINITY ? 0.f : mnew;
-    } else {
-      if (mnew == -INFINITY) return;  // nothing live yet
-    }
-    const float alpha = GROUPED && m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
-    m = mnew;
-    lsum *= alpha;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+      for (int h = 0; h < KG; ++h)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) lmx = fmaxf(lmx, sc[f * KG + h][ii]);
+    }
+    if (__builtin_amdgcn_ballot_w64(lmx * qk_abs > mth)) {  // (-inf * qk_abs is -inf: no move)
+      float mx = wave_max_over_j(lmx);
+      mx = mx == -INFINITY ? -INFINITY : mx * qk_abs;
+      const float mnew = fmaxf(m, mx);
+      // a row (GROUPED: a member's column) that has seen no key keeps m = -inf, shifts by 0 and
+      // gets probabilities exp2(-inf) = 0
+      const float alpha = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      mth = mnew + kLazyShift;
+      nm = mnew == -INFINITY ? 0.f : -mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) acc[c] *= alpha;
+    }
     typename Ops::PFrag pf[NGS];
 #pragma unroll
     for (int gi = 0; gi < NGS; ++gi) {
       f32x4 p;
 #pragma unroll
-      for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(sc[gi][ii] - mref);
+      for (int ii = 0; ii < 4; ++ii) p[ii] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[gi][ii], qk_abs, nm));
       pf[gi] = Ops::pfrag(p, lsum);
     }
 #pragma unroll
@@ -402,6 +427,7 @@ __device__ __forceinline__ void decode_stream_wave(
     for (int i = 0; i < QW / 4; ++i) {
       u32x4 v4 = src[i];
       if (!qv) v4 = (u32x4){0u, 0u, 0u, 0u};
+      v4 ^= (u32x4){qsign, qsign, qsign, qsign};
       dst[4 * i] = v4[0]; dst[4 * i + 1] = v4[1]; dst[4 * i + 2] = v4[2]; dst[4 * i + 3] = v4[3];
     }
   };
@@ -462,6 +488,8 @@ __device__ __forceinline__ void decode_stream_wave(
   }
   load_q(qw, pc);
   m = -INFINITY;
+  mth = -INFINITY;
+  nm = 0.f;
   lsum = 0.f;
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -536,6 +564,8 @@ __device__ __forceinline__ void decode_stream_wave(
     }
     if (fresh) {
       m = -INFINITY;
+      mth = -INFINITY;
+      nm = 0.f;
       lsum = 0.f;
 #pragma unroll
       for (int c = 0; c < NC; ++c) acc[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
