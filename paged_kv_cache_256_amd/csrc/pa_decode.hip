@@ -175,7 +175,7 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale, Runs runs,
     int B) {
   decode_reduce_wave<KIND, D, GROUPED, WIDE>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq,
-                                             Hkv, G, W, v_scale, runs, B);
+                                             Hkv, G, W, v_scale, runs, B, blockIdx.y);
 }
 
 // Wavefronts of a launch: the full stream (3 per CU) unless the batch holds too few units for it.
@@ -245,8 +245,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   auto reduce_kernel = grouped ? decode_reduce_kernel<KIND, D, true, false>
                        : wide  ? decode_reduce_kernel<KIND, D, false, true>
                                : decode_reduce_kernel<KIND, D, false, false>;
-  hipLaunchKernelGGL(reduce_kernel, dim3(l.W - 1), dim3(64), 0, stream, p.out, ws_ml, ws_o, plan,
-                     p.Hq, p.Hkv, G, l.W, v_scale, runs, p.B);
+  // (a grouped launch's merge has two wavefronts per boundary: they split the columns)
+  hipLaunchKernelGGL(reduce_kernel, dim3(l.W - 1, grouped ? 2 : 1), dim3(64), 0, stream, p.out, ws_ml,
+                     ws_o, plan, p.Hq, p.Hkv, G, l.W, v_scale, runs, p.B);
   return hipGetLastError();
 }
 

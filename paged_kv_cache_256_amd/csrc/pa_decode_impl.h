@@ -601,7 +601,7 @@ template <int KIND, int D, bool GROUPED = false, bool WIDE = false>
 __device__ __forceinline__ void decode_reduce_wave(
     int k, int lane, void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale,
-    Runs runs = Runs{}, int B = 0) {
+    Runs runs = Runs{}, int B = 0, int sub = 0) {
   // partials per group in flight together when a lane holds more than two quads of a row (8
   // took ~330 registers and made the merge of the 70B-shape batch 6.8 us instead of 4.6 us);
   // lanes with one or two quads keep 16 or 8 in flight
@@ -619,17 +619,21 @@ __device__ __forceinline__ void decode_reduce_wave(
   const int w0 = (int)(((x0 + 1) * W + F - 1) / F - 1);
   const int w1 = (int)(((x1 + 1) * W + F - 1) / F - 1);
   const int cuts = w1 - w0;  // boundaries cutting the run's frames, k among them
+  // A grouped run's partials hold 16 rows: each boundary then has kParts wavefronts (sub), which
+  // split its columns, so a run cut once is merged by two wavefronts.
+  constexpr int kParts = GROUPED ? 2 : 1;
   int S = 1;
-  while (2 * S <= cuts && 2 * S <= (WIDE ? D / 4 : D / 8)) S *= 2;
-  const int sl = k - w0;  // this wavefront's slice
-  if (sl >= S) return;
+  while (2 * S <= cuts && 2 * S * kParts <= (WIDE ? D / 4 : D / 8)) S *= 2;
+  if (k - w0 >= S) return;
+  const int sl = (k - w0) * kParts + sub;  // this wavefront's slice of the run's columns
+  S *= kParts;
   const int b = st.x, g = st.y;
-  // rows of the run, and a power of two at least that many for the lane layout
+  // rows of the run, and a power of two at least that many for the lane layout (a grouped run
+  // lays out all 16 rows of its partials: its row count, a load that depends on the plan, then
+  // only decides which rows are stored, and the partials' loads need not wait for it; rows past
+  // the run, never written, are merged in their own lanes and dropped)
   const int rows = GROUPED ? min(runs.size[b] * G, min(16, (B - b) * G)) : G;
-  int Gr = G;
-  if constexpr (GROUPED) {
-    while (Gr < rows) Gr *= 2;
-  }
+  const int Gr = GROUPED ? 16 : G;
   const int cq = D / (4 * S);                  // quads of a slice row
   const int lpr = cq < 64 / Gr ? cq : 64 / Gr; // lanes per row in a group
   const int qpl = cq / lpr;                    // quads per lane
@@ -654,7 +658,6 @@ __device__ __forceinline__ void decode_reduce_wave(
         const int w = wb + i * groups;
         bool has = w <= w1;
         if (!dense && has) has = F * w / W < F * (w + 1) / W;
-        if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
         const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
         const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
         const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
@@ -700,7 +703,6 @@ __device__ __forceinline__ void decode_reduce_wave(
         const int w = wb + i * groups;
         bool has = w <= w1;
         if (!dense && has) has = F * w / W < F * (w + 1) / W;
-        if constexpr (GROUPED) has = has && rr < rows;  // (rows past the run were never written)
         const int slot = (w == w0 && s0 > aw0) ? 1 : 0;
         const size_t prow = ((size_t)w * 2 + slot) * 16 + rr;
         const f32x4* src = (const f32x4*)(ws_o + prow * D + col);
