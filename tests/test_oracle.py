@@ -321,6 +321,34 @@ def test_identical_keys_give_mean_of_values():
         np.testing.assert_allclose(out[0, h], mean[h // 2], rtol=0, atol=1e-13)
 
 
+def test_dominant_key_decodes_to_its_value():
+    """When one key's scaled score (log2 of its softmax weight) exceeds every other key's by at
+    least 29, the others together carry less than L * 2^-29 of the weight, so the output is that
+    key's value to within that fraction of the largest value.  The steered spike case puts one
+    key 60 above a level in [-2, 2] and a second one 30 above it."""
+    import workloads
+    base = workloads.decode_case("dominant", 21, Hq=4, Hkv=2, D=64, bs=16, lens=[2100],
+                                 kv_dtype="f32", std=1.0, pool="scattered")
+    c = workloads.steer_scores(base, 9, "spike")
+    kc = oracle.new_cache(c.NB, c.Hkv, c.bs, c.D, "f32")
+    vc = oracle.new_cache(c.NB, c.Hkv, c.bs, c.D, "f32")
+    oracle.reshape_and_cache(kc, vc, c.pool_k, c.pool_v, np.arange(c.NB * c.bs), bs=c.bs,
+                             src_dtype="f32", kv_dtype="f32")
+    oracle.reshape_and_cache(kc, vc, c.new_k, c.new_v, c.new_slots, bs=c.bs, src_dtype="f32",
+                             kv_dtype="f32")
+    out = oracle.decode(c.q, kc, vc, c.block_tables, c.context_lens, scale=c.scale, bs=c.bs,
+                        q_dtype="f32", kv_dtype="f32")
+    t = (3 * 2099) // 4
+    slot = int(c.block_tables[0, t // c.bs]) * c.bs + t % c.bs
+    v_top = c.pool_v[slot].astype(np.float64)  # [Hkv, D]
+    tt = np.arange(2099)
+    live = c.block_tables[0, tt // c.bs].astype(np.int64) * c.bs + tt % c.bs
+    vmax = max(np.abs(c.pool_v[live]).max(), np.abs(c.new_v).max())
+    bound = 2100 * 2.0 ** -29 * vmax
+    for h in range(c.Hq):
+        np.testing.assert_allclose(out[0, h], v_top[h // c.G], rtol=0, atol=bound)
+
+
 def _brute_decode(q, K, V, scale):
     """Attention with explicit Python loops and math.exp (q [Hq, D], K/V [L, Hkv, D])."""
     Hq, D = q.shape

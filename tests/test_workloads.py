@@ -105,3 +105,58 @@ def test_named_configs_shapes(cfg):
         assert (c.B, c.Hq, c.Hkv, c.D, c.bs, c.kv_dtype) == (256, 64, 8, 128, 32, "fp8")
         assert np.all((c.context_lens >= 1024 + 64) & (c.context_lens <= 1024 + 512))
         assert 200 < len(c.copy_pairs) <= 256
+
+
+def _scaled_scores(c, b, head):
+    """Host-side scaled scores (log2 of the softmax weights, before the shift) of sequence b's
+    keys for query head `head`, from the case's raw inputs (the keys of positions < L-1 are in
+    the pool, the last one is the step's new row)."""
+    L = int(c.context_lens[b])
+    t = np.arange(L - 1)
+    slots = c.block_tables[b, t // c.bs].astype(np.int64) * c.bs + t % c.bs
+    g = head // c.G
+    k = np.concatenate([cases._as_f32(c.pool_k[slots, g], c.src_dtype),
+                        cases._as_f32(c.new_k[b:b + 1, g], c.src_dtype)]).astype(np.float64)
+    q = cases._as_f32(c.q[b, head], c.q_dtype).astype(np.float64)
+    return c.scale * np.log2(np.e) * (k @ q)
+
+
+@pytest.mark.parametrize("profile", workloads.SCORE_PROFILES)
+def test_steered_scores_follow_their_profile(profile):
+    base = workloads.decode_case("steer", 12, Hq=8, Hkv=2, D=128, bs=16, lens=[40, 700, 2100],
+                                 kv_dtype="bf16", std=0.7071, pool="scattered")
+    c = workloads.steer_scores(base, 5, profile)
+    t_max = 2099
+    for head in (0, 5):
+        s = _scaled_scores(c, 2, head)
+        if profile == "rising":
+            assert s[-1] - s[0] > 0.9 * 60.0 and np.corrcoef(np.arange(len(s)), s)[0, 1] > 0.99
+        elif profile == "falling":
+            assert s[0] - s[-1] > 0.9 * 60.0 and np.corrcoef(np.arange(len(s)), s)[0, 1] < -0.99
+        else:
+            top = (3 * t_max) // 4
+            others = np.delete(s, top)
+            assert s[top] - others.max() > 24.0  # the span/2 spike at t_max // 3 is the next
+            assert s[top] - np.median(others) > 55.0
+    # only the queries and keys change: values, tables and the poison stay
+    np.testing.assert_array_equal(c.pool_v, base.pool_v)
+    np.testing.assert_array_equal(c.block_tables, base.block_tables)
+    dead = np.ones(c.NB * c.bs, bool)
+    for b in range(c.B):
+        t = np.arange(int(c.context_lens[b]) - 1)
+        dead[c.block_tables[b, t // c.bs].astype(np.int64) * c.bs + t % c.bs] = False
+    np.testing.assert_array_equal(c.pool_k[dead], base.pool_k[dead])
+
+
+def test_steered_scores_fp8_scales_cover_the_new_keys():
+    base = workloads.decode_case("steer8", 13, Hq=8, Hkv=2, D=128, bs=32, lens=[100, 1500],
+                                 kv_dtype="fp8", std=0.7071, pool="scattered")
+    c = workloads.steer_scores(base, 6, "rising")
+    live = np.zeros(c.NB * c.bs, bool)
+    for b in range(c.B):
+        t = np.arange(int(c.context_lens[b]) - 1)
+        live[c.block_tables[b, t // c.bs].astype(np.int64) * c.bs + t % c.bs] = True
+    amax = max(np.abs(cases._as_f32(c.pool_k[live], "bf16")).max(),
+               np.abs(cases._as_f32(c.new_k, "bf16")).max())
+    assert c.k_scale == pytest.approx(amax / 448.0, rel=1e-6)
+    assert c.v_scale == base.v_scale

@@ -22,4 +22,6 @@ from .cases import (  # noqa: F401
     CONFIG_NAMES,
     POISON_K,
     POISON_V,
+    SCORE_PROFILES,
+    steer_scores,
 )

@@ -24,7 +24,7 @@ or skips a write it must make, produces a visibly wrong result.
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -469,3 +469,87 @@ def make(cfg: int, seed: int | None = None) -> DecodeCase:
         raise ValueError(f"unknown config {cfg}")
     c.meta["cfg"] = cfg
     return c
+
+# ----------------------------------------------------------------------------- steered scores
+
+SCORE_PROFILES = ("rising", "spike", "falling")
+
+
+def steer_scores(case: DecodeCase, seed: int, profile: str, span: float = 60.0) -> DecodeCase:
+    """The same case with its attention scores steered along the context.
+
+    Every query head of KV head g and every key of g lie near one unit direction u_g (queries
+    a u_g, keys beta(t) u_g, each plus N(0, 0.05^2) per element), so a key's scaled score
+    (scale * log2(e) * q.K, the softmax weight's log2) is set by a profile of its position t,
+    the same for every sequence that holds the key (shared frames hold one position):
+      rising   climbs by `span` from position 0 to the longest context's last position
+      falling  falls by `span` over the same positions
+      spike    a random level in [-2, 2], with one key `span` above it at 3/4 of the longest
+               context and one span/2 above it at 1/3
+    Tables, lengths, V, copy pairs and the poison in unwritten slots are unchanged; fp8
+    scales are recomputed from the new keys.  Only inputs are built here.
+    """
+    if profile not in SCORE_PROFILES:
+        raise ValueError(f"profile must be one of {SCORE_PROFILES}")
+    c = case
+    rng = np.random.default_rng(seed)
+    src, D, bs = c.src_dtype, c.D, c.bs
+    pos = np.full(c.NB * bs, -1, dtype=np.int64)
+    seqs = [(c.block_tables[b], int(c.context_lens[b])) for b in range(c.B)]
+    ch = c.chunk
+    if ch is not None:
+        seqs += [(ch.block_tables[i], int(ch.context_lens[i])) for i in range(ch.num_chunks)]
+    for table, L in seqs:
+        t = np.arange(L, dtype=np.int64)
+        pos[_slots(table, t, bs)] = t
+    for src_f, dst_f in c.copy_pairs:  # a copied frame holds the positions of its copy
+        a = np.arange(bs, dtype=np.int64)
+        s_sl, d_sl = src_f * bs + a, dst_f * bs + a
+        keep = pos[s_sl] < 0
+        pos[s_sl[keep]] = pos[d_sl[keep]]
+    t_max = max(1, max(L for _, L in seqs) - 1)
+    a_q = 4.0
+    per_unit = c.scale * math.log2(math.e) * a_q  # scaled score of beta = 1
+    tt = np.arange(t_max + 1, dtype=np.float64)
+    if profile == "rising":
+        target = span * tt / t_max
+    elif profile == "falling":
+        target = span * (1.0 - tt / t_max)
+    else:
+        target = rng.uniform(-2.0, 2.0, size=t_max + 1)
+        target[(3 * t_max) // 4] += span
+        target[t_max // 3] += span / 2.0
+    beta = target / per_unit
+    u = rng.standard_normal((c.Hkv, D))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+
+    def keys(p):  # p: positions [n] -> [n, Hkv, D] keys
+        k = beta[p][:, None, None] * u[None] + 0.05 * rng.standard_normal((len(p), c.Hkv, D))
+        return k.astype(np.float32)
+
+    def enc(x, dtype):
+        return x.astype(np.float32) if dtype == "f32" else _bf16_bits(x)
+
+    def queries(n):
+        g = np.arange(c.Hq) // c.G
+        x = a_q * u[g][None] + 0.05 * rng.standard_normal((n, c.Hq, D))
+        return x.astype(np.float32)
+
+    pool_k = c.pool_k.copy()
+    live = pos >= 0  # slots holding a key before the step (the step's new slots hold poison)
+    live[c.new_slots] = False
+    pool_k[live] = enc(keys(pos[live]), src)
+    new_pos = pos[c.new_slots]
+    assert (new_pos >= 0).all(), "every new row sits at a position of some sequence"
+    new_k = enc(keys(new_pos), src)
+    q = enc(queries(c.B), c.q_dtype) if c.B else c.q
+    chunk = ch
+    if ch is not None:
+        chunk = ChunkPart(q=enc(queries(ch.q.shape[0]), c.q_dtype),
+                          query_start_loc=ch.query_start_loc, context_lens=ch.context_lens,
+                          block_tables=ch.block_tables, new_rows=ch.new_rows)
+    ks, vs = c.k_scale, c.v_scale
+    if c.kv_dtype == "fp8":
+        ks, vs = _fp8_scales(pool_k, c.pool_v, live, new_k, c.new_v, src)
+    return replace(c, q=q, pool_k=pool_k, new_k=new_k, chunk=chunk, k_scale=ks, v_scale=vs,
+                   meta=dict(c.meta, profile=profile))
