@@ -146,10 +146,12 @@ size_t pa_decode_workspace_bytes(int B, int Hq, int D, int block_size, pa_dtype 
  * The batch's (sequence, kv head, frame) work is split into equal contiguous ranges over a
  * set of persistent wavefronts (three per compute unit, fewer when the host-known bound
  * B Hkv ceil(max_context_len / block_size) leaves too little work for them, so the launch
- * depends on B, Hkv, block_size and max_context_len only); a sequence cut by a range boundary is merged from
- * partial results by a second (reduce) kernel, exactly up to fp32 rounding ("CUDA Shared
- * Memory Optimization": a final normalised reduction).  The merge order is fixed, so equal
- * inputs give equal output bits.
+ * depends on B, Hkv, block_size and max_context_len only); a sequence cut by a range boundary
+ * is merged from partial results by a second (reduce) kernel, exactly up to fp32 rounding
+ * ("CUDA Shared Memory Optimization": a final normalised reduction).  The merge order is fixed,
+ * so equal inputs give equal output bits.  A small batch -- ceil(max_context_len / block_size)
+ * at most 28 and B Hkv at most the wavefront count above -- launches one wavefront per
+ * (sequence, kv head) instead, each writing its output directly, and no reduce kernel.
  */
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,

@@ -22,7 +22,10 @@
 // leaves the run to the next.  A run that lies inside one wavefront's range is finished there and
 // written to `out`; a run cut by range boundaries leaves an unnormalised partial (max, sum,
 // accumulator) in one of the two partial slots of each wavefront it touches, and the reduce
-// kernel merges them with the log-sum-exp rule.
+// kernel merges them with the log-sum-exp rule.  A small batch whose runs all fit one
+// wavefront's share by the host-known bound launches run-aligned instead: wavefront w takes run
+// (w / Hkv, w mod Hkv) whole (X of its own run, from one wave-wide sum), so nothing is cut and
+// no reduce kernel runs.
 //
 // Inside a wavefront: the frame ids of up to 64 blocks come in with one vector load (one id per
 // lane) and are broadcast with readlane; each step gathers F frames' K and V tiles straight into
@@ -156,7 +159,7 @@ __global__ __launch_bounds__(kWaves * 64, GROUPED ? 1 : kWgPerCu) void decode_st
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
-    long long NB, int cap, float qk_scale, float v_scale, Runs runs) {
+    long long NB, int cap, float qk_scale, float v_scale, Runs runs, bool aligned) {
   // Workgroups reach the 8 XCDs round-robin by id.  XCD k (workgroups k, k + 8, ...) takes the
   // k-th eighth of the ranges, so that runs next to each other in the batch -- branches that share
   // frames -- stream through the same L2.
@@ -166,7 +169,7 @@ __global__ __launch_bounds__(kWaves * 64, GROUPED ? 1 : kWgPerCu) void decode_st
   decode_stream_wave<KIND, D, BS, F, NT, GROUPED>(
       r * kWaves + uniform(threadIdx.x >> 6), gridDim.x * kWaves, out, q, k_cache,
       v_cache, block_tables, context_lens, plan, inline_plan, ws_ml, ws_o, B, mbps, Hq, Hkv, G,
-      NB, cap, qk_scale, v_scale, runs);
+      NB, cap, qk_scale, v_scale, runs, aligned);
 }
 
 template <int KIND, int D, bool GROUPED, bool WIDE>
@@ -186,6 +189,17 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
 #define PA_MIN_UNITS_PER_WAVE 16
 #endif
 constexpr long long kMinUnitsPerWave = PA_MIN_UNITS_PER_WAVE;
+
+// A batch whose runs all fit in a wavefront's minimum share, by the host-known bound (at most
+// kAlignedMaxUnits units: 28 frames), and that holds no more runs than the stream has
+// wavefronts, launches one wavefront per run instead (run-aligned): every run is then whole in
+// one wavefront, which writes its output directly, and no merge is launched.  A longer chain of
+// frames per wavefront costs less than the partials and the merge launch.
+constexpr int kAlignedMaxUnits = 2 * kMinUnitsPerWave;
+
+inline bool run_aligned(int B, int Hkv, int cap, int BS) {
+  return (long long)B * Hkv <= stream_waves() && (cap + BS - 1) / BS + kRestart <= kAlignedMaxUnits;
+}
 
 inline int launch_waves(int B, int Hkv, int cap, int BS) {
   const long long units = (long long)B * Hkv * ((cap + BS - 1) / BS + kRestart);
@@ -209,7 +223,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   constexpr int F = step_frames<KIND, D, BS>();
   const int cap = p.max_context_len < p.max_blocks_per_seq * BS ? p.max_context_len
                                                                  : p.max_blocks_per_seq * BS;
-  const int Ws = launch_waves(p.B, p.Hkv, cap, BS);
+  const bool aligned = !p.run_size && run_aligned(p.B, p.Hkv, cap, BS);
+  const int Ws = aligned ? (p.B * p.Hkv + kWaves - 1) / kWaves * kWaves
+                         : launch_waves(p.B, p.Hkv, cap, BS);
   const Layout l = layout(D, p.run_size ? std::min(Ws / kStreamWavesPerCu * kGroupedWavesPerCu,
                                                    grouped_waves())
                                         : Ws);  // within the workspace's size
@@ -223,7 +239,7 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   const Runs runs{p.run_size, p.shared_blocks};
   const bool grouped = p.run_size != nullptr;
   hipError_t e;
-  if (!inline_plan) {
+  if (!inline_plan && !aligned) {
     hipLaunchKernelGGL(decode_plan_kernel, dim3(1), dim3(1024), 0, stream, p.context_lens, plan,
                        p.B, p.Hkv, BS, cap, l.W, runs);
     e = hipGetLastError();
@@ -236,9 +252,9 @@ hipError_t launch_typed(const DecodeParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(stream_kernel, dim3(l.W / kWaves), dim3(kWaves * 64), 0, stream, p.out, p.q, (const char*)p.k_cache, (const char*)p.v_cache,
                      p.block_tables, p.context_lens, plan, inline_plan, ws_ml, ws_o, p.B,
                      p.max_blocks_per_seq, p.Hq, p.Hkv, G, (long long)p.NB, cap, qk_scale, v_scale,
-                     runs);
+                     runs, aligned);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || aligned) return e;
   // few runs against the wavefronts (a few long sequences): each run is cut into many pieces,
   // and the wide merge spreads them over more wavefronts and loads
   const bool wide = !grouped && (long long)l.W >= 16LL * p.B * p.Hkv;

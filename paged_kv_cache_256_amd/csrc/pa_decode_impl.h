@@ -166,7 +166,8 @@ __device__ __forceinline__ void decode_stream_wave(
     const char* __restrict__ v_cache, const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ context_lens, int32_t* __restrict__ plan, bool inline_plan,
     float* __restrict__ ws_ml, float* __restrict__ ws_o, int B, int mbps, int Hq, int Hkv, int G,
-    long long NB, int cap, float qk_scale, float v_scale, Runs runs = Runs{}) {
+    long long NB, int cap, float qk_scale, float v_scale, Runs runs = Runs{},
+    bool aligned = false) {
   using Ops = KvOps<KIND, D, BS>;
   constexpr int NL = Ops::NL, KG = Ops::KG, NS = Ops::NS, NC = Ops::NC, QW = Ops::QW;
   constexpr int NGS = F * KG;  // 16-key groups per step
@@ -175,26 +176,44 @@ __device__ __forceinline__ void decode_stream_wave(
 
   const int lane = threadIdx.x & 63, j = lane >> 4, n = lane & 15;
 
-  long long Ftot;
+  long long a, e;  // the wavefront's units [a, e)
   int b, g, u;  // u: unit within the run
-  if (inline_plan) {
-    const Start st = wave_plan<GROUPED>(context_lens, B, Hkv, BS, cap, W, w, lane, runs);
-    Ftot = st.F;
-    b = st.b;
-    g = st.g;
-    u = st.u;
-    if (lane == 0) {
-      ((int4*)(plan + 4))[w] = make_int4(st.b, st.g, st.u, st.su);
-      if (w == 0) plan[0] = (int)(Ftot / Hkv);
-    }
+  if (aligned) {
+    // one run per wavefront: run (b, g) = (w / Hkv, w % Hkv), whole; its first unit is Hkv times
+    // the units of the sequences before b, plus g runs of b
+    b = w / Hkv;
+    g = w - b * Hkv;
+    u = 0;
+    if (b >= B) return;
+    int pre = 0;
+    for (int bb = lane; bb < b; bb += 64) pre += run_units(blocks_of(context_lens, bb, cap, BS));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pre += __shfl_xor(pre, off);
+    const int su = run_units(blocks_of(context_lens, b, cap, BS));
+    a = (long long)Hkv * uniform(pre) + (long long)g * su;
+    e = a + su;
   } else {
-    Ftot = (long long)Hkv * plan[0];
-    const int4 st = ((const int4*)(plan + 4))[w];
-    b = uniform(st.x);
-    g = uniform(st.y);
-    u = uniform(st.z);
+    long long Ftot;
+    if (inline_plan) {
+      const Start st = wave_plan<GROUPED>(context_lens, B, Hkv, BS, cap, W, w, lane, runs);
+      Ftot = st.F;
+      b = st.b;
+      g = st.g;
+      u = st.u;
+      if (lane == 0) {
+        ((int4*)(plan + 4))[w] = make_int4(st.b, st.g, st.u, st.su);
+        if (w == 0) plan[0] = (int)(Ftot / Hkv);
+      }
+    } else {
+      Ftot = (long long)Hkv * plan[0];
+      const int4 st = ((const int4*)(plan + 4))[w];
+      b = uniform(st.x);
+      g = uniform(st.y);
+      u = uniform(st.z);
+    }
+    a = range_begin(Ftot, w, W);
+    e = range_begin(Ftot, w + 1, W);
   }
-  const long long a = range_begin(Ftot, w, W), e = range_begin(Ftot, w + 1, W);
   if (a >= e) return;
 
   // Scores scale by qk_abs >= 0; a negative scale goes into the query's sign bits (exact).  (A zero

@@ -318,11 +318,11 @@ def test_one_token_and_identical_keys_closed_forms_on_gpu():
 
 
 # The decode launch is sized from the host-known bound B Hkv (ceil(max_context_len / bs) + 4) at
-# 32 units per wavefront (whole workgroups of 4, at most 3 per compute unit): these batches give
+# 16 units per wavefront (whole workgroups of 4, at most 3 per compute unit): these batches give
 # launches from the smallest through intermediate sizes, with lengths that cut runs at many
-# wavefront boundaries.
+# wavefront boundaries.  (The first takes the run-aligned launch below: one wavefront per run.)
 LAUNCH_SIZE_CASES = [
-    # (B, longest length drawn, G): launches of 4, 8, 52, 256 and 636 wavefronts
+    # (B, longest length drawn, G)
     (1, 40, 8),
     (3, 700, 8),
     (9, 1500, 8),
@@ -339,6 +339,49 @@ def test_decode_launch_sizes(B, maxlen, G):
     c = workloads.decode_case("launch-size", 900 + B, Hq=G * Hkv, Hkv=Hkv, D=128, bs=16,
                               lens=lambda rng: rng.integers(1, maxlen + 1, size=B),
                               kv_dtype="bf16", std=0.7071)
+    g, o = GpuStep(c), OracleStep(c)
+    g.step()
+    _check_caches(g, o)
+    _check_decode(g, o)
+
+
+def _stream_wavefronts() -> int:
+    """Wavefronts of a full decode stream launch on this device: 3 per compute unit, in whole
+    workgroups of 4."""
+    return torch.cuda.get_device_properties(0).multi_processor_count * 3 // 4 * 4
+
+
+# A batch whose runs have at most 28 frames by the host-known bound (ceil(max_context_len / bs)
+# + 4 <= 32 units) and whose B Hkv runs fit in the stream's wavefronts launches one wavefront per
+# (sequence, kv head) run, each writing its output directly, and no merge.  One frame more, or
+# one run more than the stream holds, takes the split launch.  Cases on both sides of each bound;
+# every output against the oracle.
+ALIGNED_CASES = [
+    # (name, B, Hq, Hkv, D, bs, kv, longest length; B = 0: the stream's wavefronts / Hkv (+1))
+    ("aligned-f32-D64", 5, 8, 4, 64, 16, "f32", 448),
+    ("aligned-bf16", 6, 16, 2, 128, 16, "bf16", 448),
+    ("aligned-fp8-bs32", 7, 64, 8, 128, 32, "fp8", 896),
+    ("split-one-frame-past-f32-D64", 5, 8, 4, 64, 16, "f32", 449),
+    ("split-one-frame-past-fp8-bs32", 7, 64, 8, 128, 32, "fp8", 897),
+    ("aligned-runs-fill-the-stream", 0, 16, 2, 128, 16, "bf16", 448),
+    ("split-one-sequence-past-the-stream", -1, 16, 2, 128, 16, "bf16", 448),
+]
+
+
+@pytest.mark.parametrize("name,B,Hq,Hkv,D,bs,kv,longest", ALIGNED_CASES,
+                         ids=[c[0] for c in ALIGNED_CASES])
+def test_decode_run_aligned_bounds(name, B, Hq, Hkv, D, bs, kv, longest):
+    if B <= 0:
+        B = _stream_wavefronts() // Hkv + (1 if B < 0 else 0)
+    _say(f"run-aligned bound case {name}: B={B} Hkv={Hkv} longest {longest}")
+
+    def lens(rng):
+        x = rng.integers(1, longest + 1, size=B)
+        x[rng.integers(B)] = longest
+        return x
+
+    c = workloads.decode_case(name, 40 + B, Hq=Hq, Hkv=Hkv, D=D, bs=bs, lens=lens, kv_dtype=kv,
+                              std=1.0 if kv == "f32" else 0.7071, pool="scattered")
     g, o = GpuStep(c), OracleStep(c)
     g.step()
     _check_caches(g, o)
