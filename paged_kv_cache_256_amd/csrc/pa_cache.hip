@@ -4,7 +4,7 @@
 // Mapping Subsystem"): a token's slot names its frame (slot / block_size) and its offset in
 // the frame (slot % block_size).  Each workgroup stores one token: every KV head's D values
 // go to their places in the (frame, head) tile of the operand-order layout (16-byte stores for
-// K, element stores for V).  An fp8 cache stores e4m3fn(fp32(x) / scale), rounded to nearest
+// K, element stores into consecutive 16-byte lines for V).  An fp8 cache stores e4m3fn(fp32(x) / scale), rounded to nearest
 // even with saturation.
 //
 // copy_blocks implements the copy half of copy-on-write (infoisland, section 2): a frame
@@ -13,17 +13,23 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#include <type_traits>
+
 namespace pa {
 
 namespace {
 
-// One workgroup per token.  Thread t takes one 16-byte piece of the token's K row in the tile
-// layout (EPC = 16 / element-bytes consecutive head-dim values of one KV head, contiguous in the
-// K tile since a lane's fragment holds consecutive head-dim values of one key) and stores it
-// with one 16-byte store; the same head-dim values of V sit in EPC different fragments of the
-// V tile (there a fragment holds consecutive keys) and are stored one by one.
+// One workgroup per token.  K: thread t takes one 16-byte piece of the token's K row in the
+// tile layout (EPC = 16 / element-bytes consecutive head-dim values of one KV head, contiguous
+// in the K tile since a lane's fragment holds consecutive head-dim values of one key) and stores
+// it with one 16-byte store.  V: a V fragment holds consecutive keys, so the token's value for
+// head-dim index d lands in the 16-byte line of column d; thread t takes the elements t, t + 256,
+// ... of the token's V row, so that the lanes of a wavefront store into consecutive lines (a few
+// cache lines per store instruction rather than one line per lane).
+constexpr int kCacheThreads = 256;  // threads of a cache-write workgroup
+
 template <int SRC, int KV, int D, int BS>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+__global__ __launch_bounds__(kCacheThreads) void reshape_and_cache_kernel(
     const void* __restrict__ k, const void* __restrict__ v, char* __restrict__ k_cache,
     char* __restrict__ v_cache, const int64_t* __restrict__ slots, long long NB, int Hkv,
     float k_scale, float v_scale) {
@@ -33,56 +39,67 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   static_assert((D / 4) % EPC == 0, "a piece must not cross a fragment");
   constexpr int SB = SRC == KF32 ? 4 : 2;  // bytes of a source element
   typedef uint32_t SrcPiece __attribute__((ext_vector_type(EPC * SB / 4)));
+  typedef std::conditional_t<SB == 4, uint32_t, uint16_t> SrcElem;
   const long long i = blockIdx.x;
-  // The source rows do not depend on the slot: the first piece of each thread is loaded before
-  // the slot is known, so the two loads overlap instead of forming a chain.
-  const int npc = Hkv * (D / EPC);
-  SrcPiece k0 = {}, v0 = {};
-  if ((int)threadIdx.x < npc) {
-    const size_t src0 = ((size_t)i * Hkv * D + (size_t)threadIdx.x * EPC) * SB;
-    k0 = *(const SrcPiece*)((const char*)k + src0);
-    v0 = *(const SrcPiece*)((const char*)v + src0);
-  }
+  const int t = threadIdx.x;
+  // The source rows do not depend on the slot: the first K piece and V element of each thread
+  // are loaded before the slot is known, so the loads overlap instead of forming a chain.
+  const int npc = Hkv * (D / EPC), nel = Hkv * D;
+  const SrcElem* vrow = (const SrcElem*)v + (size_t)i * nel;
+  constexpr int kVB = 4;  // V elements of a thread loaded together (t + kCacheThreads u)
+  SrcPiece k0 = {};
+  SrcElem vb[kVB];
+  if (t < npc) k0 = *(const SrcPiece*)((const char*)k + ((size_t)i * nel + (size_t)t * EPC) * SB);
+#pragma unroll
+  for (int u = 0; u < kVB; ++u) vb[u] = t + kCacheThreads * u < nel ? vrow[t + kCacheThreads * u] : 0;
   const long long s = slots[i];
   if (s < 0 || s >= NB * BS) return;
   const long long f = s / BS;
   const int o = (int)(s % BS);
-  for (int pc = threadIdx.x; pc < npc; pc += blockDim.x) {
+  for (int pc = t; pc < npc; pc += kCacheThreads) {
     const int g = pc / (D / EPC), d0 = (pc % (D / EPC)) * EPC;
-    const size_t src = ((size_t)i * Hkv + g) * D + d0;
-    if (pc != (int)threadIdx.x) {
-      k0 = *(const SrcPiece*)((const char*)k + src * SB);
-      v0 = *(const SrcPiece*)((const char*)v + src * SB);
-    }
+    if (pc != t) k0 = *(const SrcPiece*)((const char*)k + (((size_t)i * Hkv + g) * D + d0) * SB);
     const char* ks = (const char*)&k0;
-    const char* vs = (const char*)&v0;
-    const size_t tile = ((size_t)f * Hkv + g) * TILE;
     u32x4 kp;
     uint8_t* kb = (uint8_t*)&kp;
-    char* vd = v_cache + tile;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      char* vdst = vd + v_tile_byte(o, d0 + e, D, EB);
       if constexpr (KV == KF32) {
         ((uint32_t*)kb)[e] = ((const uint32_t*)ks)[e];
-        *(uint32_t*)vdst = ((const uint32_t*)vs)[e];
       } else if constexpr (KV == KBF16) {
         ((uint16_t*)kb)[e] = ((const uint16_t*)ks)[e];
-        *(uint16_t*)vdst = ((const uint16_t*)vs)[e];
       } else {
-        float xk, xv;
-        if constexpr (SRC == KF32) {
-          xk = ((const float*)ks)[e];
-          xv = ((const float*)vs)[e];
-        } else {
-          xk = __uint_as_float((uint32_t)((const uint16_t*)ks)[e] << 16);
-          xv = __uint_as_float((uint32_t)((const uint16_t*)vs)[e] << 16);
-        }
+        const float xk = SRC == KF32 ? ((const float*)ks)[e]
+                                     : __uint_as_float((uint32_t)((const uint16_t*)ks)[e] << 16);
         kb[e] = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xk, k_scale));
+      }
+    }
+    *(u32x4*)(k_cache + ((size_t)f * Hkv + g) * TILE + k_tile_byte(o, d0, D, EB)) = kp;
+  }
+  for (int e0 = 0; e0 < nel; e0 += kCacheThreads * kVB) {
+    if (e0 > 0) {
+#pragma unroll
+      for (int u = 0; u < kVB; ++u) {
+        const int e = e0 + t + kCacheThreads * u;
+        vb[u] = e < nel ? vrow[e] : 0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int e = e0 + t + kCacheThreads * u;
+      if (e >= nel) break;
+      const int g = e / D, d = e % D;
+      char* vdst = v_cache + ((size_t)f * Hkv + g) * TILE + v_tile_byte(o, d, D, EB);
+      if constexpr (KV == KF32) {
+        *(uint32_t*)vdst = vb[u];
+      } else if constexpr (KV == KBF16) {
+        *(uint16_t*)vdst = vb[u];
+      } else {
+        const float xv = SRC == KF32 ? __uint_as_float((uint32_t)vb[u])
+                                     : __uint_as_float((uint32_t)vb[u] << 16);
         *(uint8_t*)vdst = (uint8_t)f32_to_e4m3fn(__fdiv_rn(xv, v_scale));
       }
     }
-    *(u32x4*)(k_cache + tile + k_tile_byte(o, d0, D, EB)) = kp;
   }
 }
 
@@ -120,7 +137,7 @@ template <int SRC, int KV, int D, int BS>
 hipError_t launch_reshape_typed(const void* k, const void* v, void* kc, void* vc,
                                 const int64_t* slots, int64_t T, int64_t NB, int Hkv,
                                 float ks, float vs, hipStream_t stream) {
-  hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KV, D, BS>), dim3((unsigned)T), dim3(256), 0,
+  hipLaunchKernelGGL((reshape_and_cache_kernel<SRC, KV, D, BS>), dim3((unsigned)T), dim3(kCacheThreads), 0,
                      stream, k, v, (char*)kc, (char*)vc, slots, (long long)NB, Hkv, ks, vs);
   return hipGetLastError();
 }
