@@ -177,8 +177,14 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(
     void* __restrict__ out, const float* __restrict__ ws_ml, const float* __restrict__ ws_o,
     const int32_t* __restrict__ plan, int Hq, int Hkv, int G, int W, float v_scale, Runs runs,
     int B) {
-  decode_reduce_wave<KIND, D, GROUPED, WIDE>(blockIdx.x, threadIdx.x, out, ws_ml, ws_o, plan, Hq,
-                                             Hkv, G, W, v_scale, runs, B, blockIdx.y);
+  // Boundaries in XCD-contiguous blocks: XCD x (workgroups x, x + 8, ...) takes the x-th block of
+  // consecutive boundaries.  The wavefronts that merge one heavily cut run by column slices are
+  // consecutive boundaries; on one XCD they read each partial row's cache lines into one L2
+  // instead of eight.
+  const int n = gridDim.x, q = n / kXcds, r = n % kXcds, x = blockIdx.x % kXcds;
+  const int k = x * q + min(x, r) + blockIdx.x / kXcds;
+  decode_reduce_wave<KIND, D, GROUPED, WIDE>(k, threadIdx.x, out, ws_ml, ws_o, plan, Hq, Hkv, G,
+                                             W, v_scale, runs, B, blockIdx.y);
 }
 
 // Wavefronts of a launch: the full stream (3 per CU) unless the batch holds too few units for it.
