@@ -136,17 +136,35 @@ __global__ __launch_bounds__(1024) void decode_plan_kernel(const int32_t* __rest
     int b = min(B, lo * per);
     const int bend = min(B, b + per);
     int su = 0;
-    for (; b < bend; ++b) {
-      su = units_of(b);
-      if (ap < cc + su) break;
-      cc += su;
-    }
-    const int off = (int)(aw - (long long)Hkv * cc);
     int4 st;
-    st.x = b;
-    st.y = su > 0 ? off / su : 0;
-    st.z = su > 0 ? off % su : 0;
-    st.w = su;
+    if (runs.size) {
+      // runs of sequences that share frames: (block lo, head g, run) order, the block being
+      // this thread's sequences (grouped_block(B) of them)
+      const int Ut = (lo < 1023 ? tex[lo + 1] : total) - cc;
+      const int rem = (int)(aw - (long long)Hkv * cc);
+      const int off = Ut > 0 ? rem % Ut : 0;
+      int c2 = 0;
+      for (; b < bend; ++b) {
+        su = units_of(b);
+        if (off < c2 + su) break;
+        c2 += su;
+      }
+      st.x = b;
+      st.y = Ut > 0 ? rem / Ut : 0;
+      st.z = off - c2;
+      st.w = su;
+    } else {
+      for (; b < bend; ++b) {
+        su = units_of(b);
+        if (ap < cc + su) break;
+        cc += su;
+      }
+      const int off = (int)(aw - (long long)Hkv * cc);
+      st.x = b;
+      st.y = su > 0 ? off / su : 0;
+      st.z = su > 0 ? off % su : 0;
+      st.w = su;
+    }
     ((int4*)(plan + 4))[w] = st;
   }
 }

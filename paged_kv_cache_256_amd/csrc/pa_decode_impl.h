@@ -109,11 +109,21 @@ __device__ inline int run_frames(const int32_t* __restrict__ context_lens, int b
   }
 }
 
+// GROUPED order: the runs are taken in blocks of grouped_block(B) consecutive sequences, and
+// inside a block head by head: (block, g, run).  The runs of one block -- branches of one prompt
+// when the batch holds a prompt's branches next to each other -- then sit next to each other for
+// each kv head, so the wavefronts that stream them at the same time read the same shared frames
+// (an L2 hit for all but the first).  The block is a lane's sequences in the in-wavefront plan
+// and a thread's in the plan kernel.
+__host__ __device__ inline int grouped_block(int B) {
+  return B <= kInlinePlanMax ? max(8, (B + 63) / 64) : (B + 1023) / 1024;
+}
+
 template <bool GROUPED = false>
 __device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int B, int Hkv, int BS,
                                   int cap, int W, int w, int lane, Runs runs = Runs{}) {
   constexpr int kPer = kInlinePlanMax / 64;
-  const int per = (B + 63) / 64;
+  const int per = GROUPED ? grouped_block(B) : (B + 63) / 64;
   int un[kPer];
   int mine = 0;
 #pragma unroll
@@ -139,6 +149,27 @@ __device__ inline Start wave_plan(const int32_t* __restrict__ context_lens, int 
   const int k = __popcll(__ballot(ex <= ap)) - 1;
   int cc = __builtin_amdgcn_readlane(ex, k);
   int bb = k * per, su = 0;
+  if constexpr (GROUPED) {
+    // (block k, head g, run): unit aw lies Hkv ex_k + g U_k + (the block's runs before it) in
+    const int Uk = __builtin_amdgcn_readlane(mine, k);  // > 0: lane k holds unit ap
+    const int rem = (int)(aw - (long long)Hkv * cc);
+    const int off = Uk > 0 ? rem % Uk : 0;
+    int c2 = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (i < per && bb < B) {
+        su = __builtin_amdgcn_readlane(un[i], k);
+        if (off < c2 + su) break;
+        c2 += su;
+        ++bb;
+      }
+    }
+    st.b = bb;
+    st.g = Uk > 0 ? rem / Uk : 0;
+    st.u = off - c2;
+    st.su = su;
+    return st;
+  }
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     if (i < per && bb < B) {
@@ -359,6 +390,7 @@ __device__ __forceinline__ void decode_stream_wave(
   };
   long long x = a;  // first unit of the next run to look at
   int rb = b, rg = g, ru = u;
+  const int gblk = grouped_block(B);  // (GROUPED order)
   // The next run piece with frames in [x, e), or false past the end of the range.
   auto find_piece = [&](Piece& pc) -> bool {
     while (x < e && rb < B) {
@@ -372,9 +404,22 @@ __device__ __forceinline__ void decode_stream_wave(
       const int pb = rb, pg = rg;
       x += units > 0 ? units : 0;
       ru = 0;
-      if (++rg == Hkv) {
-        rg = 0;
-        ++rb;
+      if constexpr (GROUPED) {
+        // the block's next run for this head, else its first run for the next head, else the
+        // next block
+        const int blk0 = pb / gblk * gblk, blk1 = min(B, blk0 + gblk);
+        if (++rb == blk1) {
+          if (++rg == Hkv) {
+            rg = 0;
+          } else {
+            rb = blk0;
+          }
+        }
+      } else {
+        if (++rg == Hkv) {
+          rg = 0;
+          ++rb;
+        }
       }
       if (f1 > f0) {
         pc.b = pb;
