@@ -423,6 +423,11 @@ def main():
         eb = {"f32": 4, "bf16": 2, "fp8": 1}[case.kv_dtype]
         extra["kv_unique_bytes_per_step"] = int(len(used)) * 2 * case.Hkv * case.bs * case.D * eb
         extra["kv_unique_gbs_decode"] = round(extra["kv_unique_bytes_per_step"] / (dec_avg * 1e-3) / 1e9, 1)
+        # achieved / frac count every sequence's context (logical bytes, above the HBM rate when
+        # shared frames come from the caches); the unique bytes are the least HBM traffic
+        roofline["bytes"] = "logical (each sequence's context; shared frames counted per sequence)"
+        roofline["unique_achieved"] = extra["kv_unique_gbs_decode"]
+        roofline["unique_frac"] = round(extra["kv_unique_gbs_decode"] / HBM_PEAK_GBS, 4)
     if args.mixed:
         fl = chunk_flops(case)
         mavg = float(chunk_ms.mean())
