@@ -22,10 +22,12 @@
 // leaves the run to the next.  A run that lies inside one wavefront's range is finished there and
 // written to `out`; a run cut by range boundaries leaves an unnormalised partial (max, sum,
 // accumulator) in one of the two partial slots of each wavefront it touches, and the reduce
-// kernel merges them with the log-sum-exp rule.  A small batch whose runs all fit one
-// wavefront's share by the host-known bound launches run-aligned instead: wavefront w takes run
-// (w / Hkv, w mod Hkv) whole (X of its own run, from one wave-wide sum), so nothing is cut and
-// no reduce kernel runs.
+// kernel merges them with the log-sum-exp rule.  (pa_decode_shared lays its runs out in blocks of
+// consecutive sequences and inside a block head by head, so that the runs of one prompt stream
+// its shared frames at the same time; the split and the merge are the same.)  A small batch whose
+// runs all fit one wavefront's share by the host-known bound launches run-aligned instead:
+// wavefront w takes run (w / Hkv, w mod Hkv) whole (X of its own run, from one wave-wide sum), so
+// nothing is cut and no reduce kernel runs.
 //
 // Inside a wavefront: the frame ids of up to 64 blocks come in with one vector load (one id per
 // lane) and are broadcast with readlane; each step gathers F frames' K and V tiles straight into
