@@ -89,6 +89,23 @@ def test_shared_prefix_runs(kv, D, bs, Hq, Hkv, P, Br, pl, tails, mr):
     _say(f"  {runs.num_runs} shared runs: max abs err {err:.2e}")
 
 
+@pytest.mark.parametrize("prompts,branches", [(75, 8), (128, 8), (97, 7)],
+                         ids=["600-seqs", "1024-seqs", "679-seqs"])
+def test_shared_prefix_runs_in_wide_plan_blocks(prompts, branches):
+    """Batches of 513-1,024 sequences planned inside the wavefronts: a plan lane then holds
+    ceil(B / 64) = 9-16 sequences, and the runs are laid out head by head within those blocks,
+    with prompts that straddle the blocks (7 branches per prompt)."""
+    c = workloads.fork_case("shared-wide", 711 + prompts, prompts=prompts, branches=branches,
+                            prompt_len=64, tail_lo=1, tail_hi=40, Hq=16, Hkv=2, D=64, bs=16,
+                            kv_dtype="fp8", std=0.7071)
+    assert 512 < c.B <= 1024
+    runs = pa.find_shared_prefixes(c.block_tables, c.context_lens, c.bs, 2)
+    g = GpuStep(c)
+    g.write()
+    err = _check(c, g, runs)
+    _say(f"{c.B} sequences, {runs.num_runs} runs: max abs err {err:.2e}")
+
+
 def test_shared_prefix_runs_above_1024_sequences():
     """1,040 sequences (130 prompts x 8 branches): the ranges are planned by the one-workgroup
     plan kernel."""
